@@ -1,0 +1,18 @@
+"""CPU oracle for MLA decode over a paged latent KV cache — TEST INFRASTRUCTURE.
+
+This package is the slow, plainly written reference the HIP path is checked against. Only the test
+suite, the package smoke check and the CPU-baseline leg of the benchmark may import it; the product
+path never calls it and shares no code with it.
+
+Everything is computed in float64 with numpy on dense, unpaged rows:
+
+- fp8.py       e4m3fn and ue8m0 decoding from their bit definitions, row dequantisation
+- attention.py absorbed (MQA-form) attention with visible sets, sink and log-sum-exp
+- merge.py     log-sum-exp merge of split partials and the sink fold
+- brute.py     pure-Python loops for tiny cases
+- mha.py       the expanded (MHA-form) computation, used only to pin the absorbed form
+- paging.py    reads a paged cache back into dense rows
+- plan.py      the split/work-unit plan, integer arithmetic
+
+Parity status of each function is stated in its module docstring.
+"""

@@ -1,0 +1,218 @@
+"""Seeded synthetic MLA decode workloads and the paged cache byte layout.
+
+Shapes follow the MLA pages: DeepSeek-V3 latent rows are 576 wide (512 latent + 64 RoPE,
+vLLM mla_attention.py module docstring, "Data-Movement Friendly Approach"); DeepSeek-V4 rows are
+512 wide (448 NoPE + 64 RoPE, HALOps MLA API, mla_attention). The fp8 page layout follows the
+HALOps kv_cache description (rows of e4m3 NoPE bytes followed by a bf16 RoPE tail, then one 8-byte
+ue8m0 scale slot per row after the rows); for 576-wide rows the same layout is used with 512 NoPE
+bytes, i.e. 640-byte rows.
+
+Nothing here computes attention: values are drawn, cast to the storage dtype by torch, and copied
+into pages. Unused pages, unused tail slots and padding bytes are filled with 0xFF, which is NaN in
+bf16, e4m3fn and ue8m0, so any read of them shows up in the outputs.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+SCALE_SLOT_BYTES = 8
+BLOCK_ROWS = 64
+
+
+def cache_layout(kv_format: str, d_qk: int, d_rope: int, page_size: int) -> dict:
+    """Byte layout of one cache page.
+
+    bf16: page_size rows of d_qk bfloat16 values.
+    fp8:  page_size rows of [d_qk - d_rope e4m3 bytes][d_rope bfloat16], then page_size 8-byte
+          scale slots (one ue8m0 byte per 64 NoPE values, zero padded); the default page stride is
+          rounded up to a multiple of the row size.
+    """
+    if kv_format == "bf16":
+        row_bytes = 2 * d_qk
+        return dict(d_nope=d_qk - d_rope, row_bytes=row_bytes, scale_offset=None,
+                    page_stride=page_size * row_bytes)
+    if kv_format == "fp8":
+        d_nope = d_qk - d_rope
+        row_bytes = d_nope + 2 * d_rope
+        raw = page_size * (row_bytes + SCALE_SLOT_BYTES)
+        stride = -(-raw // row_bytes) * row_bytes
+        return dict(d_nope=d_nope, row_bytes=row_bytes, scale_offset=page_size * row_bytes,
+                    page_stride=stride)
+    raise ValueError(f"unknown kv_format {kv_format!r}")
+
+
+@dataclasses.dataclass(frozen=True)
+class Spec:
+    name: str
+    batch: int
+    q_len: int
+    num_heads: int
+    d_qk: int = 576
+    d_v: int = 512
+    d_rope: int = 64
+    kv_format: str = "bf16"
+    page_size: int = 64
+    seqlens: Optional[Tuple[int, ...]] = None
+    len_range: Optional[Tuple[int, int]] = None
+    sm_scale: float = 1.0 / math.sqrt(192.0)
+    causal: bool = False
+    window: int = 0
+    topk: int = 0
+    sink: bool = False
+    scale_exp_range: Tuple[int, int] = (-4, 4)
+    seed: int = 0
+    plan_cus: Optional[int] = None     # compute units the plan spreads over (None: the device's)
+    spare_pages: int = 2
+    poison: bool = True
+    page_seed: Optional[int] = None    # separate seed for the page permutation (None: the main one)
+
+    @property
+    def rows_per_group(self) -> int:
+        return self.num_heads if self.topk > 0 else self.q_len * self.num_heads
+
+
+# The five workloads the MLA decode path is measured on.
+CONFIGS = {
+    1: Spec("tiny", batch=2, q_len=1, num_heads=16, d_qk=576, page_size=16, seqlens=(64, 100),
+            sm_scale=1.0 / math.sqrt(576.0), seed=1001, plan_cus=2),
+    2: Spec("dsv3_bf16", batch=64, q_len=1, num_heads=128, d_qk=576, page_size=64,
+            len_range=(1024, 8192), sm_scale=1.0 / math.sqrt(192.0), seed=1002),
+    3: Spec("dsv3_fp8", batch=64, q_len=1, num_heads=128, d_qk=576, kv_format="fp8", page_size=64,
+            len_range=(1024, 8192), sm_scale=1.0 / math.sqrt(192.0), seed=1003),
+    4: Spec("dsv4_verify", batch=32, q_len=4, num_heads=64, d_qk=512, kv_format="fp8",
+            page_size=64, len_range=(1024, 8192), sm_scale=1.0 / math.sqrt(512.0), causal=True,
+            window=128, sink=True, seed=1004),
+    5: Spec("long_sparse", batch=4, q_len=1, num_heads=128, d_qk=576, page_size=64,
+            seqlens=(131072,) * 4, sm_scale=1.0 / math.sqrt(192.0), topk=2048, seed=1005),
+}
+
+# Labelled extra shapes that show the bandwidth-bound regime the small workloads cannot.
+SUPPLEMENTARY = {
+    "s1": dataclasses.replace(CONFIGS[2], name="dsv3_bf16_h16", num_heads=16, seed=1012),
+    "s4": dataclasses.replace(CONFIGS[4], name="dsv4_verify_b512", batch=512, seed=1014),
+}
+
+
+@dataclasses.dataclass
+class Workload:
+    spec: Spec
+    seqlens: np.ndarray            # int32 [B]
+    q: torch.Tensor                # bf16 [B, Sq, H, d_qk]
+    row_offsets: np.ndarray        # int64 [B + 1]: logical rows of request b are [off[b], off[b+1])
+    rows_bf16: Optional[torch.Tensor]    # bf16 [total, d_qk]           (kv_format bf16)
+    nope_codes: Optional[torch.Tensor]   # uint8 [total, d_nope] e4m3   (kv_format fp8)
+    scale_codes: Optional[torch.Tensor]  # uint8 [total, 8] ue8m0 slot  (kv_format fp8)
+    rope_bf16: Optional[torch.Tensor]    # bf16 [total, d_rope]         (kv_format fp8)
+    cache: torch.Tensor            # uint8 [num_pages, page_stride]
+    block_table: torch.Tensor      # int32 [B, max_pages]
+    page_stride: int
+    indices: Optional[torch.Tensor]      # int32 [B, Sq, topk]
+    topk_lens: Optional[torch.Tensor]    # int32 [B * Sq]
+    sink: Optional[torch.Tensor]         # fp32 [H]
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.cache.shape[0])
+
+    def request_rows(self, b: int):
+        """Logical rows of request b in their storage dtypes (views, no copy)."""
+        a, e = int(self.row_offsets[b]), int(self.row_offsets[b + 1])
+        if self.spec.kv_format == "bf16":
+            return self.rows_bf16[a:e]
+        return self.nope_codes[a:e], self.scale_codes[a:e], self.rope_bf16[a:e]
+
+
+def _draw_seqlens(spec: Spec, g: torch.Generator) -> np.ndarray:
+    if spec.seqlens is not None:
+        assert len(spec.seqlens) == spec.batch
+        return np.asarray(spec.seqlens, dtype=np.int32)
+    lo, hi = spec.len_range
+    return torch.randint(lo, hi + 1, (spec.batch,), generator=g).numpy().astype(np.int32)
+
+
+def make(spec: Spec, seqlens: Optional[np.ndarray] = None,
+         topk_lens: Optional[np.ndarray] = None) -> Workload:
+    """Draw the workload of `spec` from its seed (CPU tensors)."""
+    g = torch.Generator().manual_seed(spec.seed)
+    if seqlens is None:
+        seqlens = _draw_seqlens(spec, g)
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    B, Sq, H, dqk, dr = spec.batch, spec.q_len, spec.num_heads, spec.d_qk, spec.d_rope
+    lay = cache_layout(spec.kv_format, dqk, dr, spec.page_size)
+    ps, row_bytes, stride = spec.page_size, lay["row_bytes"], lay["page_stride"]
+
+    q = torch.randn(B, Sq, H, dqk, generator=g).to(torch.bfloat16)
+    lens = np.maximum(seqlens.astype(np.int64), 0)
+    off = np.zeros(B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lens)
+    total = int(off[-1])
+
+    rows_bf16 = nope = scales = rope = None
+    if spec.kv_format == "bf16":
+        rows_bf16 = torch.randn(total, dqk, generator=g).to(torch.bfloat16)
+    else:
+        d_nope = lay["d_nope"]
+        ngrp = -(-d_nope // 64)
+        nope = torch.randn(total, d_nope, generator=g).to(torch.float8_e4m3fn).view(torch.uint8)
+        lo, hi = spec.scale_exp_range
+        exps = torch.randint(lo, hi + 1, (total, ngrp), generator=g)
+        scales = torch.zeros(total, SCALE_SLOT_BYTES, dtype=torch.uint8)
+        scales[:, :ngrp] = (127 + exps).to(torch.uint8)
+        rope = torch.randn(total, dr, generator=g).to(torch.bfloat16)
+
+    # Pages: each request owns ceil(L/ps) logical pages; physical ids are a random permutation.
+    npages_req = (lens + ps - 1) // ps
+    poff = np.zeros(B + 1, dtype=np.int64)
+    poff[1:] = np.cumsum(npages_req)
+    num_pages = int(poff[-1]) + spec.spare_pages
+    pg = g if spec.page_seed is None else torch.Generator().manual_seed(spec.page_seed)
+    perm = torch.randperm(num_pages, generator=pg).numpy().astype(np.int64)
+    max_pages = int(npages_req.max(initial=0)) + 1
+    spare_phys = perm[int(poff[-1])] if spec.spare_pages > 0 else perm[0]
+    block_table = np.full((B, max_pages), spare_phys, dtype=np.int32)
+    for b in range(B):
+        n = int(npages_req[b])
+        block_table[b, :n] = perm[poff[b]:poff[b] + n]
+
+    cache = np.full((num_pages, stride), 0xFF if spec.poison else 0, dtype=np.uint8)
+    if total > 0:
+        req = np.repeat(np.arange(B), lens)
+        pos = np.arange(total, dtype=np.int64) - off[req]
+        phys = perm[poff[req] + pos // ps]
+        slot = pos % ps
+        rview = np.lib.stride_tricks.as_strided(cache, shape=(num_pages, ps, row_bytes),
+                                                strides=(stride, row_bytes, 1))
+        if spec.kv_format == "bf16":
+            rview[phys, slot] = rows_bf16.view(torch.uint8).numpy().reshape(total, row_bytes)
+        else:
+            d_nope = lay["d_nope"]
+            rview[phys, slot, :d_nope] = nope.numpy()
+            rview[phys, slot, d_nope:] = rope.view(torch.uint8).numpy().reshape(total, 2 * dr)
+            sview = np.lib.stride_tricks.as_strided(
+                cache[:, lay["scale_offset"]:], shape=(num_pages, ps, SCALE_SLOT_BYTES),
+                strides=(stride, SCALE_SLOT_BYTES, 1))
+            sview[phys, slot] = scales.numpy()
+
+    indices = None
+    if spec.topk > 0:
+        idx = np.full((B, Sq, spec.topk), -1, dtype=np.int32)
+        for b in range(B):
+            for t in range(Sq):
+                L = int(lens[b])
+                k = min(L, spec.topk)
+                if k > 0:
+                    idx[b, t, :k] = torch.randperm(L, generator=g)[:k].numpy()
+        indices = torch.from_numpy(idx)
+    tl = None if topk_lens is None else torch.from_numpy(np.asarray(topk_lens, dtype=np.int32))
+    sink = torch.randn(H, generator=g, dtype=torch.float32) if spec.sink else None
+
+    return Workload(spec=spec, seqlens=seqlens, q=q, row_offsets=off, rows_bf16=rows_bf16,
+                    nope_codes=nope, scale_codes=scales, rope_bf16=rope,
+                    cache=torch.from_numpy(cache), block_table=torch.from_numpy(block_table),
+                    page_stride=stride, indices=indices, topk_lens=tl, sink=sink)
