@@ -1,0 +1,133 @@
+/*
+ * mla.h — C ABI of the MI355X (gfx950) MLA decode library.
+ *
+ * Multi-head Latent Attention decode in its absorbed, MQA-like form over a paged latent KV cache
+ * (vLLM mla_attention.py module docstring, "Data-Movement Friendly Approach": every head's query
+ * [ql_nope, q_pe] attends over rows [kv_c, k_pe] shared by all heads, and kv_c also serves as V).
+ * Three calls run in stream order, as in the FlashMLA wrapper (get_mla_metadata, then
+ * flash_mla_with_kvcache) and HALOps (mla_attention_plan, mla_attention, then the split-KV
+ * log-sum-exp combine of mla_output_proj):
+ *
+ *   mla_decode_plan  per-query-group split and work-unit metadata, computed on the device
+ *   mla_decode       paged gather, QK^T, online softmax, PV; final O/LSE for groups processed in
+ *                    one piece, fp32 partials for the others
+ *   mla_combine      log-sum-exp merge of the partials (and the sink), final O/LSE
+ *
+ * Conventions shared by every call
+ * - All pointers are device pointers unless a parameter says "host". The caller owns every buffer;
+ *   the library never allocates, frees or synchronises. `stream` is a hipStream_t (NULL = default
+ *   stream); all work is enqueued asynchronously on it, so the calls may be graph-captured.
+ * - Return value: MLA_OK (0) or a positive mla_status. Argument checks run on the host before any
+ *   launch; a failed check enqueues nothing. Launch failures are reported as MLA_ERR_LAUNCH.
+ * - Query groups: without index lists a group is one request (R = q_len * num_heads stacked query
+ *   rows, row r = t * num_heads + h); with index lists (topk > 0) a group is one (request, token)
+ *   pair g = b * q_len + t (R = num_heads rows).
+ * - Positions (vLLM MLACommonMetadata: seq_len = context_len + query_len): the q_len new tokens of
+ *   request b are its last positions, token t at pos_t = seqlens[b] - q_len + t.
+ * - Data contract (not checked): block-table entries of pages a request uses lie in
+ *   [0, num_pages) — entries outside that range are read as zero rows instead of faulting, and the
+ *   result is then unspecified; seqlens[b] <= max_pages_per_seq * page_size.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,       /* a required pointer is NULL                                      */
+  MLA_ERR_SHAPE = 2,      /* batch/q_len/heads/dims out of range or unsupported              */
+  MLA_ERR_FORMAT = 3,     /* kv_format unknown or inconsistent with the dims                 */
+  MLA_ERR_PAGE = 4,       /* page_size not a power of two, or page stride too small/unaligned */
+  MLA_ERR_MODE = 5,       /* unsupported mode combination (index lists with causal/window)   */
+  MLA_ERR_WORKSPACE = 6,  /* plan or partial buffer smaller than mla_get_workspace_size says  */
+  MLA_ERR_ALIGN = 7,      /* a pointer is not 16-byte aligned                                */
+  MLA_ERR_DEVICE = 8,     /* HIP device query failed                                         */
+  MLA_ERR_LAUNCH = 9      /* a kernel launch failed                                          */
+} mla_status;
+
+typedef enum mla_kv_format {
+  MLA_KV_BF16 = 0, /* page = page_size rows of d_qk bfloat16                                     */
+  MLA_KV_FP8 = 1   /* page = page_size rows of [d_qk - d_rope e4m3fn][d_rope bfloat16], then
+                      page_size 8-byte slots of ue8m0 scales, one per 64 NoPE values (HALOps
+                      mla_attention kv_cache layout; 640-byte rows for d_qk 576, 576 for 512)   */
+} mla_kv_format;
+
+/* The problem statement (FlashMLA wrapper I/O contract: q [B, Sq, Hq, d], k_cache
+ * (num_blocks, page_size, 1, d), block_table (B, max_blocks), cache_seqlens (B,), indices
+ * (B, Sq, topk); HALOps: head dims 512/512 with 448 NoPE + 64 RoPE, sink, windows). */
+typedef struct mla_problem {
+  int32_t batch;             /* B >= 1                                                        */
+  int32_t q_len;             /* Sq >= 1 query tokens per request                              */
+  int32_t num_heads;         /* H >= 1 query heads (one shared latent KV head)                */
+  int32_t d_qk;              /* 576 (DeepSeek-V3: 512 latent + 64 RoPE) or 512 (V4)            */
+  int32_t d_v;               /* 512: V is the first 512 columns of each (dequantised) row      */
+  int32_t d_rope;            /* 64                                                            */
+  int32_t kv_format;         /* mla_kv_format                                                 */
+  int32_t page_size;         /* rows per page, a power of two in [1, 4096]                    */
+  int64_t page_stride_bytes; /* bytes between pages: multiple of 16, >= the page's used bytes */
+  int64_t num_pages;         /* physical pages in kv_cache (>= 1)                             */
+  int32_t max_pages_per_seq; /* row stride of block_table                                     */
+  int32_t topk;              /* 0: dense; > 0: index lists of this width                      */
+  int32_t causal;            /* 1: token t sees positions <= pos_t                            */
+  int32_t window;            /* 0: none; W > 0: token t sees positions >= pos_t - W + 1       */
+} mla_problem;
+
+/* Buffer sizes for a problem planned over `num_cus` compute units (0: the current device's CU
+ * count). plan_bytes (host out): the plan buffer for mla_decode_plan. partial_bytes (host out):
+ * the fp32 split partials for mla_decode/mla_combine ([S_max][R][d_v] O then [S_max][R] LSE with
+ * S_max = groups + units). Either output pointer may be NULL. */
+int mla_get_workspace_size(const mla_problem* p, int32_t num_cus, size_t* plan_bytes,
+                           size_t* partial_bytes);
+
+/* Compute units of the current HIP device (host out). */
+int mla_device_num_cus(int32_t* num_cus);
+
+/* Plan (FlashMLA get_mla_metadata: tile scheduling metadata and split information; HALOps
+ * mla_attention_plan: a per-forward work list shared by the layers of one kind). Reads seqlens
+ * [B] int32 and, when topk > 0, the optional topk_lens [B * q_len] int32 (NULL: every token uses
+ * topk entries) on the device and writes the int32 plan: a header, per-group split ranges,
+ * per-unit split ranges, per-group (first row, row count), and split records (group, first block,
+ * end block, unit), blocks being 64 consecutive effective rows; plus a zero row used for masked
+ * rows. The plan stays valid until overwritten and may be reused by every layer of a forward. */
+int mla_decode_plan(const mla_problem* p, int32_t num_cus, const int32_t* seqlens,
+                    const int32_t* topk_lens, void* plan, size_t plan_bytes, void* stream);
+
+/* Decode (FlashMLA flash_mla_with_kvcache; HALOps mla_attention, attention part).
+ *   q           bf16 [B, Sq, H, d_qk], contiguous (RoPE already applied to its last d_rope cols)
+ *   kv_cache    paged rows in p->kv_format, page stride p->page_stride_bytes
+ *   block_table int32 [B, max_pages_per_seq]
+ *   seqlens     int32 [B] (the same array the plan read)
+ *   sm_scale    softmax scale of the QK scores
+ *   indices     int32 [B, Sq, topk] request-local positions when topk > 0, else NULL; entries
+ *               outside [0, seqlens[b]) are skipped, repeats count once per occurrence
+ *   sink        fp32 [H] per-head sink logits added once to each softmax denominator, or NULL
+ *   plan        from mla_decode_plan with the same problem and num_cus
+ *   partials    fp32 workspace of at least the partial_bytes mla_get_workspace_size gives
+ *   out         bf16 [B, Sq, H, d_v]; lse fp32 [B, H, Sq] natural-log LSE of the scaled scores
+ *               (sink included). Groups processed in one piece are written here; the rest are
+ *               written by mla_combine, which must follow on the same stream. */
+int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void* kv_cache,
+               const int32_t* block_table, const int32_t* seqlens, float sm_scale,
+               const int32_t* indices, const float* sink, const void* plan, void* partials,
+               size_t partial_bytes, void* out, float* lse, void* stream);
+
+/* Combine (vLLM merge_attn_states; HALOps mla_output_proj, split-KV LSE combine): for every group
+ * with a split count other than one, LSE = ln sum_i exp(LSE_i), O = sum_i exp(LSE_i - LSE) O_i,
+ * then the sink; a group with no rows gets O = 0 and LSE = -inf (or LSE = sink_h). */
+int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const void* partials,
+                size_t partial_bytes, const float* sink, void* out, float* lse, void* stream);
+
+/* Static description of a status code. */
+const char* mla_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

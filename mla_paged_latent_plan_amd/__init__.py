@@ -1,0 +1,130 @@
+"""MI355X (gfx950) MLA decode over a paged latent KV cache.
+
+Thin Python layer over libmla.so (include/mla.h): plan, decode and combine with the same names as
+the C ABI. Torch provides device memory and the current HIP stream; the computation is entirely in
+the HIP kernels, and the functions fail loudly when the library is missing or a tensor does not
+match the problem.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MLA_KV_BF16, MLA_KV_FP8, MLAError, Problem  # noqa: F401
+
+__all__ = ["Problem", "make_problem", "workspace_size", "mla_decode_plan", "mla_decode",
+           "mla_combine", "MLADecode", "device_num_cus", "MLAError"]
+
+
+def device_num_cus() -> int:
+    return _lib.device_num_cus()
+
+
+def make_problem(batch: int, q_len: int, num_heads: int, d_qk: int, kv_format: int,
+                 page_size: int, page_stride_bytes: int, num_pages: int, max_pages_per_seq: int,
+                 topk: int = 0, causal: bool = False, window: int = 0, d_v: int = 512,
+                 d_rope: int = 64) -> Problem:
+    return Problem(batch, q_len, num_heads, d_qk, d_v, d_rope, kv_format, page_size,
+                   page_stride_bytes, num_pages, max_pages_per_seq, topk, int(causal), window)
+
+
+def workspace_size(p: Problem, num_cus: int):
+    """(plan_bytes, partial_bytes) for a problem planned over num_cus compute units."""
+    return _lib.workspace_size(p, num_cus)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str, numel: Optional[int] = None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def mla_decode_plan(p: Problem, num_cus: int, seqlens: torch.Tensor,
+                    topk_lens: Optional[torch.Tensor], plan: torch.Tensor, stream=None) -> None:
+    lib = _lib.load()
+    _lib.check("mla_decode_plan", lib.mla_decode_plan(
+        p, num_cus, _ptr(seqlens, torch.int32, "seqlens", p.batch),
+        _ptr(topk_lens, torch.int32, "topk_lens", p.batch * p.q_len), _ptr(plan, torch.uint8, "plan"),
+        plan.numel(), _stream(stream)))
+
+
+def mla_decode(p: Problem, num_cus: int, q: torch.Tensor, kv_cache: torch.Tensor,
+               block_table: torch.Tensor, seqlens: torch.Tensor, sm_scale: float,
+               indices: Optional[torch.Tensor], sink: Optional[torch.Tensor], plan: torch.Tensor,
+               partials: torch.Tensor, out: torch.Tensor, lse: torch.Tensor, stream=None) -> None:
+    lib = _lib.load()
+    B, Sq, H = p.batch, p.q_len, p.num_heads
+    if tuple(q.shape) != (B, Sq, H, p.d_qk):
+        raise ValueError(f"q must be [{B}, {Sq}, {H}, {p.d_qk}], got {tuple(q.shape)}")
+    if tuple(out.shape) != (B, Sq, H, p.d_v):
+        raise ValueError(f"out must be [{B}, {Sq}, {H}, {p.d_v}], got {tuple(out.shape)}")
+    if kv_cache.numel() < p.num_pages * p.page_stride_bytes // kv_cache.element_size():
+        raise ValueError("kv_cache is smaller than num_pages * page_stride_bytes")
+    if tuple(block_table.shape) != (B, p.max_pages_per_seq):
+        raise ValueError("block_table must be [batch, max_pages_per_seq]")
+    if p.topk > 0 and (indices is None or tuple(indices.shape) != (B, Sq, p.topk)):
+        raise ValueError("indices must be [batch, q_len, topk] when topk > 0")
+    _lib.check("mla_decode", lib.mla_decode(
+        p, num_cus, _ptr(q, torch.bfloat16, "q"), kv_cache.data_ptr(),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(seqlens, torch.int32, "seqlens", B),
+        float(sm_scale), _ptr(indices, torch.int32, "indices"), _ptr(sink, torch.float32, "sink", H),
+        _ptr(plan, torch.uint8, "plan"), _ptr(partials, torch.uint8, "partials"), partials.numel(),
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", B * H * Sq),
+        _stream(stream)))
+
+
+def mla_combine(p: Problem, num_cus: int, plan: torch.Tensor, partials: torch.Tensor,
+                sink: Optional[torch.Tensor], out: torch.Tensor, lse: torch.Tensor,
+                stream=None) -> None:
+    lib = _lib.load()
+    _lib.check("mla_combine", lib.mla_combine(
+        p, num_cus, _ptr(plan, torch.uint8, "plan"), _ptr(partials, torch.uint8, "partials"),
+        partials.numel(), _ptr(sink, torch.float32, "sink", p.num_heads),
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+class MLADecode:
+    """Holds the plan and partial buffers of one problem and runs plan -> decode -> combine."""
+
+    def __init__(self, p: Problem, num_cus: Optional[int] = None, device="cuda"):
+        self.p = p
+        self.num_cus = device_num_cus() if num_cus is None else int(num_cus)
+        plan_bytes, part_bytes = workspace_size(p, self.num_cus)
+        self.plan = torch.empty(plan_bytes, dtype=torch.uint8, device=device)
+        self.partials = torch.empty(part_bytes, dtype=torch.uint8, device=device)
+
+    def plan_(self, seqlens: torch.Tensor, topk_lens: Optional[torch.Tensor] = None, stream=None):
+        mla_decode_plan(self.p, self.num_cus, seqlens, topk_lens, self.plan, stream)
+
+    def decode_(self, q, kv_cache, block_table, seqlens, sm_scale, out, lse, indices=None,
+                sink=None, stream=None):
+        mla_decode(self.p, self.num_cus, q, kv_cache, block_table, seqlens, sm_scale, indices, sink,
+                   self.plan, self.partials, out, lse, stream)
+        mla_combine(self.p, self.num_cus, self.plan, self.partials, sink, out, lse, stream)
+
+    def __call__(self, q, kv_cache, block_table, seqlens, sm_scale, indices=None, sink=None,
+                 topk_lens=None, stream=None):
+        p = self.p
+        out = torch.empty(p.batch, p.q_len, p.num_heads, p.d_v, dtype=torch.bfloat16,
+                          device=q.device)
+        lse = torch.empty(p.batch, p.num_heads, p.q_len, dtype=torch.float32, device=q.device)
+        self.plan_(seqlens, topk_lens, stream)
+        self.decode_(q, kv_cache, block_table, seqlens, sm_scale, out, lse, indices, sink, stream)
+        return out, lse

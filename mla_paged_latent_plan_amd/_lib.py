@@ -1,0 +1,99 @@
+"""ctypes binding of libmla.so — argument marshalling only; every step runs in the HIP kernels.
+
+Function names mirror the C ABI of include/mla.h. Torch supplies device memory and the current
+stream; tensors are passed by data pointer after host-side dtype/shape/device checks.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+from .build import LIB_PATH
+
+MLA_KV_BF16 = 0
+MLA_KV_FP8 = 1
+
+STATUS = {
+    0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_FORMAT", 4: "MLA_ERR_PAGE",
+    5: "MLA_ERR_MODE", 6: "MLA_ERR_WORKSPACE", 7: "MLA_ERR_ALIGN", 8: "MLA_ERR_DEVICE",
+    9: "MLA_ERR_LAUNCH",
+}
+
+EXPORTS = ("mla_get_workspace_size", "mla_device_num_cus", "mla_decode_plan", "mla_decode",
+           "mla_combine", "mla_strerror")
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    """struct mla_problem."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("d_qk", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("page_stride_bytes", ctypes.c_int64),
+        ("num_pages", ctypes.c_int64),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmla.so (built in-tree). Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                          "(or python -m mla_paged_latent_plan_amd.build)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(Problem)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.mla_get_workspace_size.argtypes = [P, i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.mla_device_num_cus.argtypes = [ctypes.POINTER(i32)]
+    lib.mla_decode_plan.argtypes = [P, i32, vp, vp, vp, sz, vp]
+    lib.mla_decode.argtypes = [P, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp, vp,
+                               vp]
+    lib.mla_combine.argtypes = [P, i32, vp, vp, sz, vp, vp, vp, vp]
+    lib.mla_strerror.argtypes = [ctypes.c_int]
+    lib.mla_strerror.restype = ctypes.c_char_p
+    for name in EXPORTS[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = load().mla_strerror(status).decode()
+        raise MLAError(fn, status, msg)
+
+
+def workspace_size(p: Problem, num_cus: int):
+    lib = load()
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    check("mla_get_workspace_size", lib.mla_get_workspace_size(ctypes.byref(p), num_cus,
+                                                              ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def device_num_cus() -> int:
+    n = ctypes.c_int32(0)
+    check("mla_device_num_cus", load().mla_device_num_cus(ctypes.byref(n)))
+    return n.value

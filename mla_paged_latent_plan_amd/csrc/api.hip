@@ -1,0 +1,230 @@
+// C ABI of the MLA decode library (include/mla.h): argument checks, workspace sizing, plan layout
+// and kernel dispatch. Every check runs on the host before anything is enqueued.
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+#include <math.h>
+
+using mla::PlanLayout;
+using mla::Shape;
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int query_cus(int32_t* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_DEVICE;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MLA_ERR_DEVICE;
+  *out = cus;
+  return MLA_OK;
+}
+
+// Validate a problem and derive its shape. num_cus <= 0 queries the device.
+int derive(const mla_problem* p, int32_t num_cus, Shape* sh) {
+  if (p == nullptr || sh == nullptr) return MLA_ERR_NULL;
+  if (p->batch < 1 || p->q_len < 1 || p->num_heads < 1) return MLA_ERR_SHAPE;
+  if (p->d_v != 512 || p->d_rope != 64) return MLA_ERR_SHAPE;
+  if (p->d_qk != 576 && p->d_qk != 512) return MLA_ERR_SHAPE;
+  if (p->kv_format != MLA_KV_BF16 && p->kv_format != MLA_KV_FP8) return MLA_ERR_FORMAT;
+  if (!is_pow2(p->page_size) || p->page_size > 4096) return MLA_ERR_PAGE;
+  if (p->topk < 0 || p->window < 0 || (p->causal != 0 && p->causal != 1)) return MLA_ERR_MODE;
+  if (p->topk > 0 && (p->causal != 0 || p->window != 0)) return MLA_ERR_MODE;
+  if (p->max_pages_per_seq < 1 || p->num_pages < 1 || p->num_pages > INT32_MAX) return MLA_ERR_PAGE;
+  const int64_t d_nope = p->d_qk - p->d_rope;
+  const int64_t row_bytes = (p->kv_format == MLA_KV_BF16) ? 2LL * p->d_qk : d_nope + 2LL * p->d_rope;
+  const int64_t used = (int64_t)p->page_size * (row_bytes + (p->kv_format == MLA_KV_FP8 ? 8 : 0));
+  if (p->page_stride_bytes < used || (p->page_stride_bytes & 15) != 0) return MLA_ERR_PAGE;
+
+  const int64_t R = (p->topk > 0) ? (int64_t)p->num_heads : (int64_t)p->q_len * p->num_heads;
+  const int64_t G = (p->topk > 0) ? (int64_t)p->batch * p->q_len : (int64_t)p->batch;
+  if (R > 65536 || G > mla::kMaxGroups) return MLA_ERR_SHAPE;
+  if (num_cus <= 0) {
+    int rc = query_cus(&num_cus);
+    if (rc != MLA_OK) return rc;
+  }
+  int m_tile = 0, fixed = 0;
+  mla::tile_params((int)R, &m_tile, &fixed);
+  sh->B = p->batch;
+  sh->Sq = p->q_len;
+  sh->H = p->num_heads;
+  sh->R = (int)R;
+  sh->G = (int)G;
+  sh->m_tile = m_tile;
+  sh->fixed = fixed;
+  sh->m_tiles = (int)((R + m_tile - 1) / m_tile);
+  sh->U = num_cus / sh->m_tiles;
+  if (sh->U < 1) sh->U = 1;
+  sh->d_qk = p->d_qk;
+  sh->d_rope = p->d_rope;
+  sh->fmt = p->kv_format;
+  sh->page_size = p->page_size;
+  int lg = 0;
+  while ((1 << lg) < p->page_size) ++lg;
+  sh->ps_log2 = lg;
+  sh->max_pages = p->max_pages_per_seq;
+  sh->topk = p->topk;
+  sh->causal = p->causal;
+  sh->window = p->window;
+  sh->page_stride = p->page_stride_bytes;
+  sh->num_pages = p->num_pages;
+  sh->row_bytes = row_bytes;
+  sh->s_max = (int64_t)sh->G + sh->U;
+  return MLA_OK;
+}
+
+size_t partial_size(const Shape& sh) {
+  return (size_t)sh.s_max * (size_t)sh.R * (size_t)(mla::kDv + 1) * sizeof(float);
+}
+
+int launch_rc(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int mla_device_num_cus(int32_t* num_cus) {
+  if (num_cus == nullptr) return MLA_ERR_NULL;
+  return query_cus(num_cus);
+}
+
+int mla_get_workspace_size(const mla_problem* p, int32_t num_cus, size_t* plan_bytes,
+                           size_t* partial_bytes) {
+  Shape sh;
+  int rc = derive(p, num_cus, &sh);
+  if (rc != MLA_OK) return rc;
+  if (plan_bytes) *plan_bytes = (size_t)PlanLayout::make(sh.G, sh.U).bytes;
+  if (partial_bytes) *partial_bytes = partial_size(sh);
+  return MLA_OK;
+}
+
+int mla_decode_plan(const mla_problem* p, int32_t num_cus, const int32_t* seqlens,
+                    const int32_t* topk_lens, void* plan, size_t plan_bytes, void* stream) {
+  Shape sh;
+  int rc = derive(p, num_cus, &sh);
+  if (rc != MLA_OK) return rc;
+  if (seqlens == nullptr || plan == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(plan)) return MLA_ERR_ALIGN;
+  const PlanLayout lay = PlanLayout::make(sh.G, sh.U);
+  if (plan_bytes < (size_t)lay.bytes) return MLA_ERR_WORKSPACE;
+  mla::PlanArgs a;
+  a.seqlens = seqlens;
+  a.topk_lens = (sh.topk > 0) ? topk_lens : nullptr;
+  a.plan = static_cast<int32_t*>(plan);
+  a.lay = lay;
+  a.B = sh.B;
+  a.Sq = sh.Sq;
+  a.R = sh.R;
+  a.G = sh.G;
+  a.U = sh.U;
+  a.m_tiles = sh.m_tiles;
+  a.m_tile = sh.m_tile;
+  a.fixed = sh.fixed;
+  a.topk = sh.topk;
+  a.window = sh.window;
+  return launch_rc(mla::launch_plan(a, static_cast<hipStream_t>(stream)));
+}
+
+int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void* kv_cache,
+               const int32_t* block_table, const int32_t* seqlens, float sm_scale,
+               const int32_t* indices, const float* sink, const void* plan, void* partials,
+               size_t partial_bytes, void* out, float* lse, void* stream) {
+  Shape sh;
+  int rc = derive(p, num_cus, &sh);
+  if (rc != MLA_OK) return rc;
+  if (q == nullptr || kv_cache == nullptr || block_table == nullptr || seqlens == nullptr ||
+      plan == nullptr || out == nullptr || lse == nullptr)
+    return MLA_ERR_NULL;
+  if (sh.topk > 0 && indices == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(plan) || !aligned16(out) ||
+      (partials != nullptr && !aligned16(partials)))
+    return MLA_ERR_ALIGN;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return MLA_ERR_SHAPE;
+  const size_t need = partial_size(sh);
+  if (partials == nullptr || partial_bytes < need) return MLA_ERR_WORKSPACE;
+  if (sh.fmt != MLA_KV_BF16) return MLA_ERR_FORMAT;  // fp8 rows: not available yet
+  const PlanLayout lay = PlanLayout::make(sh.G, sh.U);
+  mla::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.cache = static_cast<const uint8_t*>(kv_cache);
+  a.block_table = block_table;
+  a.seqlens = seqlens;
+  a.indices = (sh.topk > 0) ? indices : nullptr;
+  a.sink = sink;
+  a.plan = static_cast<const int32_t*>(plan);
+  a.zero_row = static_cast<const uint8_t*>(plan) + lay.zero_row_bytes_off;
+  a.part_o = static_cast<float*>(partials);
+  a.part_lse = a.part_o + (size_t)sh.s_max * sh.R * mla::kDv;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.page_stride = sh.page_stride;
+  a.num_pages = sh.num_pages;
+  a.row_bytes = sh.row_bytes;
+  a.grp_ptr_off = lay.grp_ptr;
+  a.unit_ptr_off = lay.unit_ptr;
+  a.grp_rows_off = lay.grp_rows;
+  a.splits_off = lay.splits;
+  a.B = sh.B;
+  a.Sq = sh.Sq;
+  a.H = sh.H;
+  a.R = sh.R;
+  a.G = sh.G;
+  a.U = sh.U;
+  a.m_tiles = sh.m_tiles;
+  a.ps_log2 = sh.ps_log2;
+  a.max_pages = sh.max_pages;
+  a.topk = sh.topk;
+  a.causal = sh.causal;
+  a.window = sh.window;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  return launch_rc(mla::launch_decode(a, sh, static_cast<hipStream_t>(stream)));
+}
+
+int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const void* partials,
+                size_t partial_bytes, const float* sink, void* out, float* lse, void* stream) {
+  Shape sh;
+  int rc = derive(p, num_cus, &sh);
+  if (rc != MLA_OK) return rc;
+  if (plan == nullptr || out == nullptr || lse == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(plan) || !aligned16(out) || (partials != nullptr && !aligned16(partials)))
+    return MLA_ERR_ALIGN;
+  if (partials == nullptr || partial_bytes < partial_size(sh)) return MLA_ERR_WORKSPACE;
+  const PlanLayout lay = PlanLayout::make(sh.G, sh.U);
+  mla::CombineArgs a;
+  a.plan = static_cast<const int32_t*>(plan);
+  a.part_o = static_cast<const float*>(partials);
+  a.part_lse = a.part_o + (size_t)sh.s_max * sh.R * mla::kDv;
+  a.sink = sink;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.grp_ptr_off = lay.grp_ptr;
+  a.B = sh.B;
+  a.Sq = sh.Sq;
+  a.H = sh.H;
+  a.R = sh.R;
+  a.G = sh.G;
+  a.sparse = sh.topk > 0;
+  return launch_rc(mla::launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* mla_strerror(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "unsupported or out-of-range shape";
+    case MLA_ERR_FORMAT: return "unknown or unsupported kv_format";
+    case MLA_ERR_PAGE: return "invalid page size, page stride or page count";
+    case MLA_ERR_MODE: return "unsupported mode combination";
+    case MLA_ERR_WORKSPACE: return "workspace buffer too small";
+    case MLA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MLA_ERR_DEVICE: return "HIP device query failed";
+    case MLA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

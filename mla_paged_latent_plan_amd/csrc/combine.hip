@@ -1,0 +1,103 @@
+// mla_combine kernel: log-sum-exp merge of split partials (vLLM merge_attn_states; HALOps
+// mla_output_proj, "split-KV LSE combine"), then the attention sink.
+//
+// For each query group whose split count is not one: LSE = ln sum_i exp(LSE_i) and
+// O = sum_i exp(LSE_i - LSE) O_i over the group's splits; a split with no visible rows carries
+// LSE_i = -inf and no weight (vLLM neutralize_empty_context_partials). The sink (HALOps attn_sink)
+// then adds exp(sink_h) once to the denominator. A group with no splits at all gets O = 0 and
+// LSE = -inf, or LSE = sink_h with a sink. Groups with exactly one split were finished by
+// mla_decode and are skipped.
+//
+// Launch: one workgroup of 256 threads per (group, 4 query rows); 64 threads per row, each
+// owning 8 consecutive columns, so partial rows are read as contiguous 2 KB lines.
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ uint16_t f2bf(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int g = blockIdx.y;
+  const int s0 = a.plan[a.grp_ptr_off + g];
+  const int s1 = a.plan[a.grp_ptr_off + g + 1];
+  const int ns = s1 - s0;
+  if (ns == 1) return;
+  const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= a.R) return;
+  const int c = (threadIdx.x & 63) * 8;
+
+  int b, t, h;
+  if (a.sparse) {
+    b = g / a.Sq;
+    t = g % a.Sq;
+    h = r;
+  } else {
+    b = g;
+    t = r / a.H;
+    h = r % a.H;
+  }
+
+  float mx = kNegInf;
+  for (int s = s0; s < s1; ++s) mx = fmaxf(mx, a.part_lse[(int64_t)s * a.R + r]);
+  float wsum = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (mx != kNegInf) {
+    for (int s = s0; s < s1; ++s) {
+      const float ls = a.part_lse[(int64_t)s * a.R + r];
+      const float w = (ls == kNegInf) ? 0.f : __expf(ls - mx);
+      wsum += w;
+      const float4* src = reinterpret_cast<const float4*>(a.part_o + ((int64_t)s * a.R + r) * kDv + c);
+      const float4 v0 = src[0], v1 = src[1];
+      acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
+      acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
+    }
+  }
+  float lse, scale;
+  if (wsum > 0.f) {
+    lse = mx + __logf(wsum);
+    scale = 1.f / wsum;
+  } else {
+    lse = kNegInf;
+    scale = 0.f;
+  }
+  if (a.sink != nullptr) {
+    const float sk = a.sink[h];
+    if (lse == kNegInf) {
+      lse = sk;
+      scale = 0.f;
+    } else {
+      const float m2 = fmaxf(lse, sk);
+      const float lse2 = m2 + __logf(__expf(lse - m2) + __expf(sk - m2));
+      scale *= __expf(lse - lse2);
+      lse = lse2;
+    }
+  }
+  uint4 w;
+  w.x = (uint32_t)f2bf(acc[0] * scale) | ((uint32_t)f2bf(acc[1] * scale) << 16);
+  w.y = (uint32_t)f2bf(acc[2] * scale) | ((uint32_t)f2bf(acc[3] * scale) << 16);
+  w.z = (uint32_t)f2bf(acc[4] * scale) | ((uint32_t)f2bf(acc[5] * scale) << 16);
+  w.w = (uint32_t)f2bf(acc[6] * scale) | ((uint32_t)f2bf(acc[7] * scale) << 16);
+  *reinterpret_cast<uint4*>(a.out + ((int64_t)g * a.R + r) * kDv + c) = w;
+  if ((threadIdx.x & 63) == 0) a.lse[((int64_t)b * a.H + h) * a.Sq + t] = lse;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  if (a.G <= 0) return hipSuccess;
+  dim3 grid((a.R + kRowsPerBlock - 1) / kRowsPerBlock, a.G);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

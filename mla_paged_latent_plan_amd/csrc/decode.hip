@@ -1,0 +1,603 @@
+// mla_decode kernel for gfx950: absorbed-form MLA decode over a paged latent cache.
+//
+// What it computes (vLLM mla_attention.py module docstring, "Data-Movement Friendly Approach"):
+// all heads of a query group attend over the same latent rows, K = [kv_c, k_pe] (d_qk wide) and
+// V = kv_c (the first 512 columns). Per split (a run of 64-row blocks of one group, from the
+// plan) a workgroup produces either the final bf16 O and natural-log LSE, or an fp32 partial
+// (O normalised by its own denominator, LSE without the sink) for mla_combine.
+//
+// Mapping onto CDNA4:
+// - Workgroup = 4 waves; the group's query rows (heads, times tokens when q_len > 1) are the
+//   N dimension of S^T = K Q^T and of O^T = V^T P^T, so one LDS copy of a KV block serves every
+//   head of the tile. A wave owns HW query rows (Q^T kept in VGPRs) and KVW rows of each block;
+//   waves that split a block's rows (WN > 1) keep separate softmax states merged at the end.
+// - KV rows are gathered page by page with global_load_lds_dwordx4 (no VGPR staging), one row
+//   (1 KB) or eight RoPE tails per instruction, into a double-buffered LDS stage of 64 rows.
+//   The latent part uses a padded row stride (1040 B); S^T tile row m maps to LDS row rho(m) so
+//   that both the QK^T operand reads (ds_read_b128) and the transposed V reads
+//   (ds_read_b64_tr_b16) hit distinct banks with affine addresses. RoPE tails are XOR-swizzled.
+// - QK^T and PV are v_mfma_f32_16x16x32_bf16 (16x16x16 when a wave owns only 16 rows of a
+//   block). The S^T accumulator layout is directly the B operand of PV, so P never leaves
+//   registers; V^T comes from the transposed LDS read.
+// - Online softmax in base 2 with a lazily moved reference maximum: O is rescaled only when a
+//   row's maximum grows by more than 2^8, which keeps the 256 accumulator registers untouched in
+//   the common case. Row statistics are per lane (the head index runs along lanes).
+// - Masked rows (past the group's rows, invalid indices, pages outside the cache) are gathered
+//   from the plan's zero row, so no NaN from unused cache bytes can reach the accumulators.
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kThreads = 256;
+constexpr int kRowStrideA = 1040;            // latent part: 1 KB + 16 B padding
+constexpr int kStageA = kBlockRows * kRowStrideA;
+constexpr int kStageB = kBlockRows * 128;    // RoPE tails (64 bf16), XOR-swizzled
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kTau = 8.0f;                 // lazy rescale threshold (log2 units)
+
+template <int HW_, int WN_, int DQK_>
+struct Cfg {
+  static constexpr int HW = HW_;             // query rows per wave
+  static constexpr int WN = WN_;             // waves sharing a head tile (splitting block rows)
+  static constexpr int WM = 4 / WN;          // head tiles per workgroup
+  static constexpr int DQK = DQK_;
+  static constexpr int M_TILE = HW * WM;
+  static constexpr int NT = HW / 16;
+  static constexpr int KVW = kBlockRows / WN;
+  static constexpr int SUB = KVW >= 32 ? 32 : 16;  // rows per softmax/PV step
+  static constexpr int NSUB = KVW / SUB;
+  static constexpr int KT = SUB / 16;              // 16-row S^T tiles per step
+  static constexpr int KS = DQK / 32;
+  static constexpr bool HAS_B = DQK > 512;
+  static constexpr int STAGE = kStageA + (HAS_B ? kStageB : 0);
+  static constexpr int LDS = 2 * STAGE;
+  static_assert(WN == 1 || 4 * HW * kDv * 4 + 8 * HW * 4 <= LDS,
+                "merge scratch must fit in the stage buffers");
+};
+
+// S^T tile row m (MFMA lane index) -> LDS row within the 16-row tile.
+__device__ __forceinline__ int rho(int m) {
+  return 2 * (4 * ((m >> 2) & 1) + (m & 3)) + (m >> 3);
+}
+__device__ __forceinline__ int swz_b(int row) { return (row >> 1) & 7; }
+
+typedef LDS_AS uint8_t* lds_ptr;
+
+__device__ __forceinline__ bf16x8 lds_read_b128(lds_ptr base, uint32_t off) {
+  return *reinterpret_cast<const LDS_AS bf16x8*>(base + off);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr(lds_ptr base, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<LDS_AS bf16x4*>(base + off));
+}
+
+__device__ __forceinline__ float wave_max_groups(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_groups(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
+  uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint16_t f2bf(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Per-lane row descriptor for one stage (lane = row within the 64-row block).
+struct RowInfo {
+  int j;       // logical position (dense) or index value (sparse)
+  int valid;
+};
+
+template <class C>
+struct Decoder {
+  const DecodeArgs& a;
+  lds_ptr sm;
+  int lane, wave, wm, wn;
+  // current split
+  int g, b, L, j0, n, kb, ke;
+
+  __device__ Decoder(const DecodeArgs& args, lds_ptr base) : a(args), sm(base) {
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    wm = wave / C::WN;
+    wn = wave % C::WN;
+  }
+
+  __device__ __forceinline__ uint32_t stage_a(int st) const { return st * C::STAGE; }
+  __device__ __forceinline__ uint32_t stage_b(int st) const { return st * C::STAGE + kStageA; }
+
+  // Position (and validity) of block row `lane` of block `blk`: loads the index for sparse.
+  __device__ __forceinline__ RowInfo row_pos(int blk) const {
+    RowInfo r;
+    const int k = blk * kBlockRows + lane;
+    r.valid = (blk < ke) && (k < n);
+    if (a.topk > 0) {
+      int idx = -1;
+      if (r.valid) idx = a.indices[(int64_t)g * a.topk + k];
+      r.j = idx;
+      r.valid = r.valid && idx >= 0 && idx < L;
+    } else {
+      r.j = j0 + k;
+    }
+    // rows past the block table's capacity are read as zeros instead of indexing past it
+    r.valid = r.valid && (r.j >> a.ps_log2) < a.max_pages;
+    return r;
+  }
+  __device__ __forceinline__ int row_page(const RowInfo& r) const {
+    int page = 0;
+    if (r.valid) page = a.block_table[(int64_t)b * a.max_pages + (r.j >> a.ps_log2)];
+    return page;
+  }
+  __device__ __forceinline__ uint64_t row_base(const RowInfo& r, int page, int* valid) const {
+    const bool ok = r.valid && page >= 0 && (int64_t)page < a.num_pages;
+    *valid = ok;
+    if (!ok) return (uint64_t)(uintptr_t)a.zero_row;
+    const int slot = r.j & ((1 << a.ps_log2) - 1);
+    return (uint64_t)(uintptr_t)(a.cache + (int64_t)page * a.page_stride + (int64_t)slot * a.row_bytes);
+  }
+
+  // Issue the LDS-DMA of one 64-row block into stage `st`; `base` is this lane's row address.
+  __device__ __forceinline__ void issue_stage(int st, uint64_t base) const {
+    const uint32_t sa = stage_a(st);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = wave * 16 + i;
+      const uint64_t rb = readlane64(base, r);
+      const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 16 * lane;
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + r * kRowStrideA),
+                                       16, 0, 0);
+    }
+    if constexpr (C::HAS_B) {
+      const uint32_t sb = stage_b(st);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int k = wave * 2 + kk;
+        const int r = 8 * k + (lane >> 3);
+        const int c = (lane & 7) ^ swz_b(r);
+        const uint32_t lo = __shfl((uint32_t)base, r, 64);
+        const uint32_t hi = __shfl((uint32_t)(base >> 32), r, 64);
+        const uint64_t rb = ((uint64_t)hi << 32) | lo;
+        const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 1024 + 16 * c;
+        __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sb + k * 1024), 16,
+                                         0, 0);
+      }
+    }
+  }
+
+  __device__ void run_split(int s, int mt) {
+    const int32_t* plan = a.plan;
+    const int32_t* rec = plan + a.splits_off + 4 * (int64_t)s;
+    g = rec[0];
+    kb = rec[1];
+    ke = rec[2];
+    j0 = plan[a.grp_rows_off + 2 * g];
+    n = plan[a.grp_rows_off + 2 * g + 1];
+    const int nsplit = plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g];
+    b = (a.topk > 0) ? g / a.Sq : g;
+    L = a.seqlens[b];
+
+    const int row0 = mt * C::M_TILE + wm * C::HW;  // first query row of this wave
+    const int nl = lane & 15, gl = lane >> 4;
+
+    // ---- Q^T operand registers ------------------------------------------------------------
+    bf16x8 qr[C::NT][C::KS];
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      const int r = row0 + nt * 16 + nl;
+      const bool ok = r < a.R;
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(
+          a.q + ((int64_t)g * a.R + (ok ? r : 0)) * C::DQK + 8 * gl);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        bf16x8 v = src[4 * ks];
+        if (!ok) v = bf16x8{};
+        qr[nt][ks] = v;
+      }
+    }
+    // query position of each lane's rows (dense masks)
+    int qpos[C::NT];
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      const int r = row0 + nt * 16 + nl;
+      const int t = (a.topk > 0) ? 0 : (r / a.H);
+      qpos[nt] = L - a.Sq + t;
+    }
+
+    float m_ref[C::NT], l_acc[C::NT];
+    f32x4 o[C::NT][kDv / 16];
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      m_ref[nt] = kNegInf;
+      l_acc[nt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < kDv / 16; ++dt) o[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- prologue: row info for kb (now), kb+1 (pages), kb+2 (positions) -----------------
+    RowInfo r0 = row_pos(kb);
+    int valid0;
+    uint64_t base0 = row_base(r0, row_page(r0), &valid0);
+    uint64_t vmask_next = __ballot(valid0);
+    issue_stage(0, base0);
+    RowInfo r1 = row_pos(kb + 1);
+    int page1 = row_page(r1);
+    RowInfo r2 = row_pos(kb + 2);
+
+    const bool dense_mask = (a.topk == 0) && (a.causal || a.window > 0);
+    for (int blk = kb; blk < ke; ++blk) {
+      const int cur = (blk - kb) & 1;
+      const uint64_t vmask = vmask_next;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (blk + 1 < ke) {
+        int v1;
+        const uint64_t base1 = row_base(r1, page1, &v1);
+        vmask_next = __ballot(v1);
+        issue_stage(cur ^ 1, base1);
+        r1 = r2;
+        page1 = row_page(r1);
+        r2 = row_pos(blk + 3);
+      }
+
+      const uint32_t sa = stage_a(cur);
+      const uint32_t sb = stage_b(cur);
+#pragma unroll
+      for (int sub = 0; sub < C::NSUB; ++sub) {
+        const int rbase = wn * C::KVW + sub * C::SUB;  // first stage row of this step
+
+        // ---- S^T = K Q^T -------------------------------------------------------------------
+        f32x4 sacc[C::KT][C::NT];
+#pragma unroll
+        for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+          for (int nt = 0; nt < C::NT; ++nt) sacc[kt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        uint32_t kaddr[C::KT];
+#pragma unroll
+        for (int kt = 0; kt < C::KT; ++kt)
+          kaddr[kt] = sa + (rbase + 16 * kt + rho(nl)) * kRowStrideA + 16 * gl;
+        // K operand of step ks for tile kt: latent part (affine) or RoPE tail (swizzled)
+        auto k_operand = [&](int kt, int ks) -> bf16x8 {
+          if (ks < 16) return lds_read_b128(sm, kaddr[kt] + 64 * ks);
+          const int row = rbase + 16 * kt + rho(nl);
+          const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
+          return lds_read_b128(sm, sb + row * 128 + 16 * c);
+        };
+        // one step of operands in flight ahead of the MFMAs that consume the previous one
+        bf16x8 ka[2][C::KT];
+#pragma unroll
+        for (int kt = 0; kt < C::KT; ++kt) ka[0][kt] = k_operand(kt, 0);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          if (ks + 1 < C::KS) {
+#pragma unroll
+            for (int kt = 0; kt < C::KT; ++kt) ka[(ks + 1) & 1][kt] = k_operand(kt, ks + 1);
+          }
+#pragma unroll
+          for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt)
+              sacc[kt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kt], qr[nt][ks],
+                                                                     sacc[kt][nt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- masks -------------------------------------------------------------------------
+        const bool tail = blk * kBlockRows + rbase + C::SUB > n;
+        bool need_mask = tail || dense_mask;
+        if (a.topk > 0) need_mask = (vmask != ~0ull);
+        if (need_mask) {
+#pragma unroll
+          for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int row = rbase + 16 * kt + rho(4 * gl + e);
+              const int k = blk * kBlockRows + row;
+#pragma unroll
+              for (int nt = 0; nt < C::NT; ++nt) {
+                bool ok;
+                if (a.topk > 0) {
+                  ok = (vmask >> row) & 1;
+                } else {
+                  const int j = j0 + k;
+                  ok = k < n;
+                  if (a.causal) ok = ok && j <= qpos[nt];
+                  if (a.window > 0) ok = ok && j >= qpos[nt] - a.window + 1;
+                }
+                if (!ok) sacc[kt][nt][e] = kNegInf;
+              }
+            }
+        }
+
+        // ---- online softmax (base 2, lazy reference max) ------------------------------------
+        bool need_rescale = false;
+        float m_new[C::NT];
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+          float mx = kNegInf;
+#pragma unroll
+          for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kt][nt][e]);
+          mx = wave_max_groups(mx);
+          m_new[nt] = mx * a.scale_log2;  // -inf stays -inf (scale > 0)
+          need_rescale |= (m_new[nt] > m_ref[nt] + kTau);
+        }
+        if (__any(need_rescale)) {
+#pragma unroll
+          for (int nt = 0; nt < C::NT; ++nt) {
+            const bool up = m_new[nt] > m_ref[nt] + kTau;
+            const float alpha = up ? exp2f(m_ref[nt] - m_new[nt]) : 1.f;  // m_ref=-inf -> 0
+            if (up) m_ref[nt] = m_new[nt];
+            l_acc[nt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < kDv / 16; ++dt) {
+              o[nt][dt] *= alpha;
+              __builtin_amdgcn_sched_barrier(0);  // one tile out of the accumulators at a time
+            }
+          }
+        }
+        // P = exp2(s * scale_log2 - m_ref), packed as the B operand of PV
+        bf16x8 p8[C::NT];
+        bf16x4 p4[C::NT];
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+          const float mu = (m_ref[nt] == kNegInf) ? 0.f : m_ref[nt];
+          float lsum = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < C::KT; ++kt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pv = exp2f(__builtin_fmaf(sacc[kt][nt][e], a.scale_log2, -mu));
+              lsum += pv;
+              const __bf16 pb = (__bf16)pv;
+              if constexpr (C::SUB == 32) p8[nt][kt * 4 + e] = pb;
+              else p4[nt][e] = pb;
+            }
+          }
+          l_acc[nt] += lsum;
+        }
+
+        // ---- O^T += V^T P^T ----------------------------------------------------------------
+        // lane (i, g): transposed-read row rho(4g + i/4) of the tile, columns 16 dt + 4 (i % 4)
+        const uint32_t vbase = sa + (rbase + rho(4 * gl + ((lane & 15) >> 2))) * kRowStrideA +
+                               8 * (lane & 3);
+        if constexpr (C::SUB == 32) {
+          auto v_operand = [&](int dt) -> bf16x8 {
+            const uint32_t ad = vbase + 32 * dt;
+            const bf16x4 v0 = lds_read_tr(sm, ad);
+            const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
+            return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          };
+          bf16x8 va[2];
+          va[0] = v_operand(0);
+#pragma unroll
+          for (int dt = 0; dt < kDv / 16; ++dt) {
+            if (dt + 1 < kDv / 16) va[(dt + 1) & 1] = v_operand(dt + 1);
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt)
+              o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt & 1], p8[nt], o[nt][dt],
+                                                                  0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          bf16x4 va[2];
+          va[0] = lds_read_tr(sm, vbase);
+#pragma unroll
+          for (int dt = 0; dt < kDv / 16; ++dt) {
+            if (dt + 1 < kDv / 16) va[(dt + 1) & 1] = lds_read_tr(sm, vbase + 32 * (dt + 1));
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt)
+              o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt & 1], p4[nt], o[nt][dt],
+                                                                    0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+    __syncthreads();  // all waves done with the stage buffers (reused by the merge below)
+
+    // ---- epilogue ----------------------------------------------------------------------------
+    const bool final_out = (nsplit == 1);
+    if constexpr (C::WN == 1) {
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) {
+        const float lt = wave_sum_groups(l_acc[nt]);
+        const int r = row0 + nt * 16 + nl;
+        write_row(s, r, m_ref[nt], lt, o[nt], final_out);
+      }
+    } else {
+      // merge the WN partial states of each head tile through LDS
+      LDS_AS float* so = reinterpret_cast<LDS_AS float*>(sm);  // [wave][HW][512] O
+      LDS_AS float* sml = so + 4 * C::HW * kDv;                 // [wave][HW] m, then l
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) {
+        const float lt = wave_sum_groups(l_acc[nt]);
+        const int hrow = nt * 16 + nl;
+        if (gl == 0) {
+          sml[wave * C::HW + hrow] = m_ref[nt];
+          sml[4 * C::HW + wave * C::HW + hrow] = lt;
+        }
+#pragma unroll
+        for (int dt = 0; dt < kDv / 16; ++dt) {
+          LDS_AS f32x4* dst =
+              reinterpret_cast<LDS_AS f32x4*>(so + (wave * C::HW + hrow) * kDv + dt * 16 + 4 * gl);
+          *dst = o[nt][dt];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __syncthreads();
+      // each thread: rows x float4 columns of the M_TILE x 512 output
+      for (int it = threadIdx.x; it < C::M_TILE * (kDv / 4); it += kThreads) {
+        const int row = it / (kDv / 4);
+        const int c4 = it % (kDv / 4);
+        const int tm = row / C::HW, hrow = row % C::HW;
+        float ms[C::WN], ls[C::WN];
+        float mstar = kNegInf;
+#pragma unroll
+        for (int w = 0; w < C::WN; ++w) {
+          const int wv = tm * C::WN + w;
+          ms[w] = sml[wv * C::HW + hrow];
+          ls[w] = sml[4 * C::HW + wv * C::HW + hrow];
+          mstar = fmaxf(mstar, ms[w]);
+        }
+        float lstar = 0.f;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < C::WN; ++w) {
+          const int wv = tm * C::WN + w;
+          const float cw = (ms[w] == kNegInf) ? 0.f : exp2f(ms[w] - mstar);
+          lstar += cw * ls[w];
+          const f32x4 v = *reinterpret_cast<LDS_AS f32x4*>(so + (wv * C::HW + hrow) * kDv + 4 * c4);
+          acc += cw * v;
+        }
+        const int r = mt * C::M_TILE + row;
+        if (r < a.R) store_vec(s, r, 4 * c4, mstar, lstar, acc, final_out, c4 == 0);
+      }
+      __syncthreads();  // scratch reused by the next split
+    }
+  }
+
+  // Final or partial output of one query row from a lane's O^T registers (WN == 1 path).
+  __device__ __forceinline__ void write_row(int s, int r, float m2, float l, const f32x4* orow,
+                                            bool final_out) const {
+    if (r >= a.R) return;
+    const int gl = lane >> 4;
+    float lse_nat, scale;
+    row_norm(r, m2, l, final_out, &lse_nat, &scale);
+    if (final_out) {
+      uint16_t* dst = a.out + ((int64_t)g * a.R + r) * kDv + 4 * gl;
+#pragma unroll
+      for (int dt = 0; dt < kDv / 16; ++dt) {
+        const f32x4 v = orow[dt] * scale;
+        uint2 w;
+        w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+        w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+        *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (gl == 0) a.lse[lse_index(r)] = lse_nat;
+    } else {
+      float* dst = a.part_o + ((int64_t)s * a.R + r) * kDv + 4 * gl;
+#pragma unroll
+      for (int dt = 0; dt < kDv / 16; ++dt) {
+        *reinterpret_cast<f32x4*>(dst + 16 * dt) = orow[dt] * scale;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (gl == 0) a.part_lse[(int64_t)s * a.R + r] = lse_nat;
+    }
+  }
+
+  // Four consecutive columns of one row (merged path).
+  __device__ __forceinline__ void store_vec(int s, int r, int col, float m2, float l, f32x4 v,
+                                            bool final_out, bool write_lse) const {
+    float lse_nat, scale;
+    row_norm(r, m2, l, final_out, &lse_nat, &scale);
+    v *= scale;
+    if (final_out) {
+      uint2 w;
+      w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      *reinterpret_cast<uint2*>(a.out + ((int64_t)g * a.R + r) * kDv + col) = w;
+      if (write_lse) a.lse[lse_index(r)] = lse_nat;
+    } else {
+      *reinterpret_cast<f32x4*>(a.part_o + ((int64_t)s * a.R + r) * kDv + col) = v;
+      if (write_lse) a.part_lse[(int64_t)s * a.R + r] = lse_nat;
+    }
+  }
+
+  // LSE (natural log) and output scale of a row; the sink is folded in for final outputs.
+  __device__ __forceinline__ void row_norm(int r, float m2, float l, bool final_out, float* lse_nat,
+                                           float* scale) const {
+    const float kLn2 = 0.69314718055994530942f;
+    if (l > 0.f) {
+      float lse = (m2 + __log2f(l)) * kLn2;
+      float sc = 1.f / l;
+      if (final_out && a.sink != nullptr) {
+        const float sk = a.sink[head_of(r)];
+        const float mx = fmaxf(lse, sk);
+        const float lse2 = mx + __logf(__expf(lse - mx) + __expf(sk - mx));
+        sc *= __expf(lse - lse2);
+        lse = lse2;
+      }
+      *lse_nat = lse;
+      *scale = sc;
+    } else {
+      *scale = 0.f;
+      *lse_nat = (final_out && a.sink != nullptr) ? a.sink[head_of(r)] : kNegInf;
+    }
+  }
+
+  __device__ __forceinline__ int head_of(int r) const { return (a.topk > 0) ? r : r % a.H; }
+  __device__ __forceinline__ int64_t lse_index(int r) const {
+    int bb, t, h;
+    if (a.topk > 0) {
+      bb = g / a.Sq;
+      t = g % a.Sq;
+      h = r;
+    } else {
+      bb = g;
+      t = r / a.H;
+      h = r % a.H;
+    }
+    return ((int64_t)bb * a.H + h) * a.Sq + t;
+  }
+};
+
+template <class C>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+  const lds_ptr base = (lds_ptr)lds;
+  const int m_tiles = a.m_tiles;
+  const int unit = blockIdx.x / m_tiles;
+  const int mt = blockIdx.x % m_tiles;
+  if (unit >= a.U) return;
+  const int s0 = a.plan[a.unit_ptr_off + unit];
+  const int s1 = a.plan[a.unit_ptr_off + unit + 1];
+  Decoder<C> d(a, base);
+  for (int s = s0; s < s1; ++s) d.run_split(s, mt);
+}
+
+// The kernel's row tile may be smaller than the plan's: the grid then holds one workgroup per
+// (unit, kernel row tile), all of a unit's workgroups walking the same splits.
+template <class C>
+hipError_t launch_cfg(DecodeArgs a, hipStream_t s) {
+  a.m_tiles = (a.R + C::M_TILE - 1) / C::M_TILE;
+  const int64_t grid = (int64_t)a.U * a.m_tiles;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_kernel<C>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DQK>
+hipError_t launch_dqk(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
+  if (sh.R <= 16) return launch_cfg<Cfg<16, 4, DQK>>(a, s);
+  if (sh.R <= 32) return launch_cfg<Cfg<16, 2, DQK>>(a, s);
+  return launch_cfg<Cfg<16, 1, DQK>>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
+  if (sh.fmt != 0) return hipErrorNotSupported;
+  return sh.d_qk == 576 ? launch_dqk<576>(a, sh, s) : launch_dqk<512>(a, sh, s);
+}
+
+}  // namespace mla

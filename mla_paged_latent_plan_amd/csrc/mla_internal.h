@@ -1,0 +1,100 @@
+// Internal definitions shared by the plan, decode and combine kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// ---- plan layout (int32 words) -------------------------------------------------------------
+// header[16] | grp_ptr[G+1] | unit_ptr[U+1] | grp_rows[2G] | splits[4*(G+U)] | pad to 256 B |
+// zero row (kZeroRowBytes)
+constexpr int32_t kPlanMagic = 0x4D4C4131;
+constexpr int kHeaderWords = 16;
+constexpr int kBlockRows = 64;       // rows per block (one LDS stage)
+constexpr int kZeroRowBytes = 2048;  // >= the widest row (1152 B)
+constexpr int kMaxGroups = 8192;     // plan kernel keeps per-group state in LDS
+constexpr int kDv = 512;
+
+enum { H_MAGIC = 0, H_G, H_U, H_S, H_R, H_MTILES, H_MTILE, H_QUOTA, H_FIXED, H_TOTAL, H_SMAX };
+
+struct PlanLayout {
+  int64_t G, U;
+  int64_t grp_ptr, unit_ptr, grp_rows, splits, words;  // word offsets
+  int64_t zero_row_bytes_off, bytes;                    // byte offsets / size
+  static PlanLayout make(int64_t G, int64_t U) {
+    PlanLayout l;
+    l.G = G;
+    l.U = U;
+    l.grp_ptr = kHeaderWords;
+    l.unit_ptr = l.grp_ptr + G + 1;
+    l.grp_rows = l.unit_ptr + U + 1;
+    l.splits = l.grp_rows + 2 * G;
+    l.words = l.splits + 4 * (G + U);
+    l.zero_row_bytes_off = ((l.words * 4 + 255) / 256) * 256;
+    l.bytes = l.zero_row_bytes_off + kZeroRowBytes;
+    return l;
+  }
+};
+
+// Kernel tile for R stacked query rows per group: (M_TILE, FIXED split overhead in blocks).
+inline void tile_params(int R, int* m_tile, int* fixed) {
+  if (R <= 16) { *m_tile = 16; *fixed = 1; }
+  else if (R <= 32) { *m_tile = 32; *fixed = 2; }
+  else if (R <= 64) { *m_tile = 64; *fixed = 2; }
+  else { *m_tile = 128; *fixed = 4; }
+}
+
+struct Shape {  // derived, validated problem shape
+  int B, Sq, H, R, G, m_tile, fixed, m_tiles, U, d_qk, d_rope, fmt, page_size, ps_log2;
+  int max_pages, topk, causal, window;
+  int64_t page_stride, num_pages, row_bytes, s_max;
+};
+
+// ---- kernel argument blocks ----------------------------------------------------------------
+struct PlanArgs {
+  const int32_t* seqlens;
+  const int32_t* topk_lens;
+  int32_t* plan;
+  PlanLayout lay;
+  int B, Sq, R, G, U, m_tiles, m_tile, fixed, topk, window;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint8_t* cache;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const int32_t* indices;
+  const float* sink;
+  const int32_t* plan;
+  const uint8_t* zero_row;
+  float* part_o;
+  float* part_lse;
+  uint16_t* out;
+  float* lse;
+  int64_t page_stride, num_pages, row_bytes;
+  int64_t grp_ptr_off, unit_ptr_off, grp_rows_off, splits_off;
+  int B, Sq, H, R, G, U, m_tiles, ps_log2, max_pages, topk, causal, window;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+struct CombineArgs {
+  const int32_t* plan;
+  const float* part_o;
+  const float* part_lse;
+  const float* sink;
+  uint16_t* out;
+  float* lse;
+  int64_t grp_ptr_off;
+  int B, Sq, H, R, G;
+  int sparse;
+};
+
+// Launchers (defined in the .hip files).
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, const Shape& sh, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,146 @@
+"""Shared helpers of the GPU tests: move a workload to the device, run the HIP path through the
+C ABI, evaluate the oracle on the same inputs and measure the difference."""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from oracle import attention as oatt
+from oracle import fp8 as ofp8
+from oracle import plan as oplan
+
+# Parity bar for the decode outputs (bf16 O against the float64 oracle).
+REL_L2 = 5e-3
+MAX_ABS = 2e-2
+LSE_ABS = 1e-3
+
+
+def problem_of(wl, mla):
+    s = wl.spec
+    return mla.make_problem(
+        batch=s.batch, q_len=s.q_len, num_heads=s.num_heads, d_qk=s.d_qk,
+        kv_format=mla.MLA_KV_BF16 if s.kv_format == "bf16" else mla.MLA_KV_FP8,
+        page_size=s.page_size, page_stride_bytes=wl.page_stride, num_pages=wl.num_pages,
+        max_pages_per_seq=int(wl.block_table.shape[1]), topk=s.topk, causal=s.causal,
+        window=s.window, d_v=s.d_v, d_rope=s.d_rope)
+
+
+@dataclasses.dataclass
+class DeviceInputs:
+    q: torch.Tensor
+    cache: torch.Tensor
+    block_table: torch.Tensor
+    seqlens: torch.Tensor
+    indices: Optional[torch.Tensor]
+    topk_lens: Optional[torch.Tensor]
+    sink: Optional[torch.Tensor]
+
+
+def to_device(wl, device="cuda") -> DeviceInputs:
+    return DeviceInputs(
+        q=wl.q.to(device),
+        cache=wl.cache.to(device),
+        block_table=wl.block_table.to(device),
+        seqlens=torch.from_numpy(wl.seqlens).to(device),
+        indices=None if wl.indices is None else wl.indices.to(device),
+        topk_lens=None if wl.topk_lens is None else wl.topk_lens.to(device),
+        sink=None if wl.sink is None else wl.sink.to(device))
+
+
+def run_gpu(wl, num_cus: Optional[int] = None, dev: Optional[DeviceInputs] = None):
+    """plan + decode + combine through the C ABI; returns (out bf16, lse fp32, plan words) on CPU."""
+    import mla_paged_latent_plan_amd as mla
+    dev = dev or to_device(wl)
+    p = problem_of(wl, mla)
+    if num_cus is None:
+        num_cus = wl.spec.plan_cus or mla.device_num_cus()
+    runner = mla.MLADecode(p, num_cus)
+    out, lse = runner(dev.q, dev.cache, dev.block_table, dev.seqlens, wl.spec.sm_scale,
+                      indices=dev.indices, sink=dev.sink, topk_lens=dev.topk_lens)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), runner.plan.cpu(), num_cus
+
+
+def dense_rows(wl, b: int) -> np.ndarray:
+    """Oracle-side float64 rows of request b, decoded from the logical (unpaged) rows."""
+    r = wl.request_rows(b)
+    if wl.spec.kv_format == "bf16":
+        return r.to(torch.float64).numpy()
+    nope, scales, rope = r
+    return ofp8.dequant_rows(nope.numpy(), scales.numpy(), rope.to(torch.float64).numpy())
+
+
+def dense_rows_at(wl, b: int, J: np.ndarray) -> np.ndarray:
+    """Oracle-side float64 rows J (request-local positions) of request b."""
+    off = int(wl.row_offsets[b])
+    J = np.asarray(J, dtype=np.int64) + off
+    if wl.spec.kv_format == "bf16":
+        return wl.rows_bf16[torch.from_numpy(J)].to(torch.float64).numpy()
+    t = torch.from_numpy(J)
+    return ofp8.dequant_rows(wl.nope_codes[t].numpy(), wl.scale_codes[t].numpy(),
+                             wl.rope_bf16[t].to(torch.float64).numpy())
+
+
+def oracle_of(wl, requests: Optional[Sequence[int]] = None):
+    """Oracle O [b, Sq, H, 512] and LSE [b, H, Sq] for the listed requests (all by default)."""
+    s = wl.spec
+    req = list(range(s.batch)) if requests is None else list(requests)
+    q = wl.q[req].to(torch.float64).numpy()
+    seq = wl.seqlens[req]
+    idx = None if wl.indices is None else wl.indices[req].numpy()
+    tl = None
+    if wl.topk_lens is not None:
+        tl = wl.topk_lens.numpy().reshape(s.batch, s.q_len)[req].reshape(-1)
+    sink = None if wl.sink is None else wl.sink.to(torch.float64).numpy()
+    if idx is None:
+        return oatt.mla_decode(q, lambda i: dense_rows(wl, req[i]), seq, s.sm_scale, s.d_v,
+                               s.causal, s.window, None, None, sink)
+    # index lists: decode only the listed rows of each (request, token)
+    B, Sq, H = len(req), s.q_len, s.num_heads
+    O = np.zeros((B, Sq, H, s.d_v))
+    LSE = np.zeros((B, H, Sq))
+    for i, b in enumerate(req):
+        L = int(seq[i])
+        for t in range(Sq):
+            n = None if tl is None else int(tl[i * Sq + t])
+            J = oatt.visible_sparse(L, idx[i, t], n)
+            K = dense_rows_at(wl, b, J)
+            o, l = oatt.attend(q[i, t], K, s.sm_scale, s.d_v, sink)
+            O[i, t] = o
+            LSE[i, :, t] = l
+    return O, LSE
+
+
+def plan_words(wl, num_cus: int) -> np.ndarray:
+    s = wl.spec
+    tl = None if wl.topk_lens is None else wl.topk_lens.numpy()
+    return oplan.build_plan(wl.seqlens, s.q_len, s.num_heads, num_cus, s.topk, s.window, tl)
+
+
+def metrics(out: torch.Tensor, lse: torch.Tensor, O_ref: np.ndarray, L_ref: np.ndarray) -> dict:
+    o = out.to(torch.float64).numpy()
+    l = lse.to(torch.float64).numpy()
+    diff = o - O_ref
+    nref = np.linalg.norm(O_ref)
+    finite_ref = np.isfinite(L_ref)
+    lse_match_inf = bool(np.all(np.isneginf(l[~finite_ref]))) if (~finite_ref).any() else True
+    lse_err = float(np.max(np.abs(l[finite_ref] - L_ref[finite_ref]))) if finite_ref.any() else 0.0
+    return dict(
+        rel_l2=float(np.linalg.norm(diff) / nref) if nref > 0 else float(np.linalg.norm(diff)),
+        max_abs=float(np.max(np.abs(diff))) if diff.size else 0.0,
+        lse_max_abs=lse_err,
+        lse_inf_ok=lse_match_inf,
+        finite=bool(np.all(np.isfinite(o))),
+    )
+
+
+def assert_parity(m: dict, rel_l2=REL_L2, max_abs=MAX_ABS, lse_abs=LSE_ABS, ctx=""):
+    assert m["finite"], f"{ctx} non-finite outputs {m}"
+    assert m["lse_inf_ok"], f"{ctx} empty rows must give LSE -inf {m}"
+    assert m["rel_l2"] <= rel_l2, f"{ctx} rel-L2 {m}"
+    assert m["max_abs"] <= max_abs, f"{ctx} max-abs {m}"
+    assert m["lse_max_abs"] <= lse_abs, f"{ctx} LSE {m}"

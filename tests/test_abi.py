@@ -1,0 +1,121 @@
+"""The C ABI library (no GPU needed): it loads, exports every function include/mla.h declares, and
+rejects invalid arguments on the host before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+import mla_paged_latent_plan_amd as mla
+from mla_paged_latent_plan_amd import _lib, build
+
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.LIB_PATH):
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {build.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not exported"
+
+
+def good(**kw):
+    base = dict(batch=2, q_len=1, num_heads=16, d_qk=576, kv_format=0, page_size=16,
+                page_stride_bytes=16 * 1152, num_pages=10, max_pages_per_seq=8)
+    base.update(kw)
+    return mla.make_problem(**base)
+
+
+def ws(p, cus=256):
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    return _lib.load().mla_get_workspace_size(ctypes.byref(p), cus, ctypes.byref(a),
+                                              ctypes.byref(b)), a.value, b.value
+
+
+def test_workspace_sizes(lib):
+    rc, plan_b, part_b = ws(good(), 256)
+    assert rc == 0
+    G, U = 2, 256
+    words = 16 + (G + 1) + (U + 1) + 2 * G + 4 * (G + U)
+    assert plan_b == ((words * 4 + 255) // 256) * 256 + 2048
+    assert part_b == (G + U) * 16 * 513 * 4
+    # 128 heads: one 128-row tile per group, U = cus
+    rc, _, part_b = ws(good(num_heads=128), 256)
+    assert rc == 0 and part_b == (2 + 256) * 128 * 513 * 4
+    # 4 tokens x 64 heads = 256 rows -> 2 tiles, U = 128
+    rc, _, part_b = ws(good(num_heads=64, q_len=4, causal=1, window=128), 256)
+    assert rc == 0 and part_b == (2 + 128) * 256 * 513 * 4
+    # index lists: groups are (request, token) pairs of H rows
+    rc, _, part_b = ws(good(num_heads=128, q_len=2, topk=64), 256)
+    assert rc == 0 and part_b == (4 + 256) * 128 * 513 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 2), (dict(q_len=0), 2), (dict(num_heads=0), 2), (dict(d_qk=320), 2),
+    (dict(d_v=448), 2), (dict(d_rope=32), 2), (dict(kv_format=2), 3), (dict(page_size=24), 4),
+    (dict(page_size=0), 4), (dict(page_size=8192), 4), (dict(page_stride_bytes=100), 4),
+    (dict(page_stride_bytes=16 * 1152 - 16), 4), (dict(num_pages=0), 4),
+    (dict(max_pages_per_seq=0), 4), (dict(topk=-1), 5), (dict(window=-3), 5),
+    (dict(causal=2), 5), (dict(topk=8, causal=1), 5), (dict(topk=8, window=4), 5),
+    (dict(batch=9000, topk=4), 2),
+    (dict(kv_format=1, page_stride_bytes=16 * 640), 4),
+])
+def test_invalid_problems_rejected(lib, kw, status):
+    rc, _, _ = ws(good(**kw))
+    assert rc == status, (kw, rc)
+
+
+def test_fp8_layout_accepted(lib):
+    rc, _, _ = ws(good(kv_format=1, page_stride_bytes=16 * 648))
+    assert rc == 0
+    rc, _, _ = ws(good(kv_format=1, d_qk=512, page_size=64, page_stride_bytes=37440))
+    assert rc == 0
+
+
+def test_host_checks_before_launch(lib):
+    p = good()
+    vp = ctypes.c_void_p
+    # null seqlens / plan
+    assert lib.mla_decode_plan(ctypes.byref(p), 256, None, None, vp(4096), 1 << 20, None) == 1
+    assert lib.mla_decode_plan(ctypes.byref(p), 256, vp(4096), None, None, 1 << 20, None) == 1
+    # misaligned plan, plan too small
+    assert lib.mla_decode_plan(ctypes.byref(p), 256, vp(4096), None, vp(4100), 1 << 20, None) == 7
+    assert lib.mla_decode_plan(ctypes.byref(p), 256, vp(4096), None, vp(4096), 64, None) == 6
+    # decode: null q, bad scale, small partials
+    args = [ctypes.byref(p), 256, None, vp(4096), vp(4096), vp(4096), ctypes.c_float(0.1), None,
+            None, vp(4096), vp(4096), 1 << 30, vp(4096), vp(4096), None]
+    assert lib.mla_decode(*args) == 1
+    args[2] = vp(4096)
+    args[6] = ctypes.c_float(-1.0)
+    assert lib.mla_decode(*args) == 2
+    args[6] = ctypes.c_float(0.1)
+    args[11] = 16
+    assert lib.mla_decode(*args) == 6
+    # index lists without indices
+    ps = good(topk=8)
+    args[0] = ctypes.byref(ps)
+    args[11] = 1 << 30
+    assert lib.mla_decode(*args) == 1
+    # combine: null out
+    assert lib.mla_combine(ctypes.byref(p), 256, vp(4096), vp(4096), 1 << 30, None, None, vp(4096),
+                           None) == 1
+    assert lib.mla_strerror(6) == b"workspace buffer too small"

@@ -1,0 +1,133 @@
+"""GPU parity of the HIP path (plan, decode, combine through the C ABI) against the CPU oracle.
+
+Every case runs on seeded synthetic inputs whose unused cache bytes are NaN, so a read outside the
+visible rows shows up as a non-finite output."""
+
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import CONFIGS, Spec, make
+
+import mla_harness as H
+
+pytestmark = pytest.mark.gpu
+
+S = 1.0 / math.sqrt(192.0)
+
+CASES = {
+    "cfg1_tiny": (CONFIGS[1], None),
+    "h128_edges": (Spec("h128_edges", batch=6, q_len=1, num_heads=128, page_size=64,
+                        seqlens=(1, 63, 64, 65, 700, 2001), sm_scale=S, seed=11), None),
+    "h16_page16": (Spec("h16_page16", batch=7, q_len=1, num_heads=16, page_size=16,
+                        seqlens=(0, 1, 15, 130, 511, 1000, 64), sm_scale=S, seed=12), None),
+    "h32_page32": (Spec("h32_page32", batch=3, q_len=1, num_heads=32, page_size=32,
+                        seqlens=(5, 300, 129), sm_scale=S, seed=13), None),
+    "h64_sq2_causal": (Spec("h64_sq2_causal", batch=4, q_len=2, num_heads=64, page_size=64,
+                            seqlens=(1, 2, 777, 130), causal=True, sm_scale=S, seed=14), None),
+    "h24_odd_heads": (Spec("h24_odd_heads", batch=2, q_len=1, num_heads=24, page_size=64,
+                           seqlens=(100, 333), sm_scale=S, seed=18), None),
+    "d512_window_sink": (Spec("d512_window_sink", batch=4, q_len=4, num_heads=16, d_qk=512,
+                              page_size=64, seqlens=(3, 131, 1000, 4), causal=True, window=128,
+                              sink=True, sm_scale=1 / math.sqrt(512), seed=15), None),
+    "sparse_h128": (Spec("sparse_h128", batch=2, q_len=1, num_heads=128, page_size=64,
+                         seqlens=(5000, 3), topk=300, sm_scale=S, seed=16), None),
+    "sparse_h16_lens": (Spec("sparse_h16_lens", batch=2, q_len=2, num_heads=16, page_size=16,
+                             seqlens=(400, 90), topk=128, sm_scale=S, seed=17),
+                        np.array([100, 0, 128, 64])),
+}
+
+
+def _make(name):
+    spec, tl = CASES[name]
+    wl = make(spec, topk_lens=tl)
+    if wl.indices is not None:
+        # invalid entries: negative and past the sequence end are skipped
+        idx = wl.indices.numpy()
+        idx[0, 0, ::7] = -1
+        idx[0, 0, 3::11] = int(wl.seqlens[0]) + 5
+        wl.indices = torch.from_numpy(idx)
+    return wl
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("cus", ["device", "one", "many"])
+def test_parity(name, cus):
+    wl = _make(name)
+    num_cus = {"device": None, "one": 1, "many": 1024}[cus]
+    print(f"[gpu] parity {name} cus={cus}", flush=True)
+    out, lse, plan, used = H.run_gpu(wl, num_cus)
+    O, L = H.oracle_of(wl)
+    m = H.metrics(out, lse, O, L)
+    print(f"[gpu]   {m}", flush=True)
+    H.assert_parity(m, ctx=f"{name}/{cus}")
+    want = H.plan_words(wl, used)
+    got = plan.view(torch.int32).numpy()[:len(want)]
+    assert np.array_equal(got, want), f"plan differs for {name}/{cus}"
+
+
+def test_page_permutation_bitwise():
+    spec = dataclasses.replace(CASES["h128_edges"][0], page_seed=1)
+    a = make(spec)
+    b = make(dataclasses.replace(spec, page_seed=2))
+    assert not torch.equal(a.block_table, b.block_table)
+    print("[gpu] page permutation", flush=True)
+    oa, la, _, _ = H.run_gpu(a)
+    ob, lb, _, _ = H.run_gpu(b)
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+    assert torch.equal(la, lb)
+
+
+def test_repeat_bitwise():
+    wl = _make("h16_page16")
+    print("[gpu] repeat", flush=True)
+    o1, l1, _, _ = H.run_gpu(wl)
+    o2, l2, _, _ = H.run_gpu(wl)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_uniform_scores_exact_mean():
+    """q = 0 gives O = mean of the visible V rows and LSE = ln(count) exactly (closed form)."""
+    spec = Spec("zero_q", batch=3, q_len=1, num_heads=16, page_size=16, seqlens=(1, 37, 256),
+                sm_scale=S, seed=21)
+    wl = make(spec)
+    wl.q = torch.zeros_like(wl.q)
+    out, lse, _, _ = H.run_gpu(wl)
+    for b in range(3):
+        L = int(wl.seqlens[b])
+        mean = wl.request_rows(b).to(torch.float64)[:, :512].mean(dim=0)
+        np.testing.assert_allclose(out[b, 0].to(torch.float64).numpy(),
+                                   np.broadcast_to(mean.numpy(), (16, 512)), atol=2e-2, rtol=1e-2)
+        np.testing.assert_allclose(lse[b, :, 0].numpy(), math.log(L), atol=1e-4)
+
+
+def test_sparse_arange_equals_dense():
+    spec = Spec("sp_eq", batch=2, q_len=1, num_heads=128, page_size=64, seqlens=(300, 64),
+                sm_scale=S, seed=22)
+    dense = make(spec)
+    sp = make(dataclasses.replace(spec, topk=300))
+    idx = np.full((2, 1, 300), -1, dtype=np.int32)
+    idx[0, 0, :] = np.arange(300)
+    idx[1, 0, :64] = np.arange(64)
+    sp.indices = torch.from_numpy(idx)
+    od, ld, _, _ = H.run_gpu(dense)
+    os_, ls, _, _ = H.run_gpu(sp)
+    m = H.metrics(os_, ls, od.to(torch.float64).numpy(), ld.to(torch.float64).numpy())
+    assert m["max_abs"] <= 1e-2 and m["lse_max_abs"] <= 1e-4, m
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_full_size_configs(cfg):
+    """The benchmark workloads at their full sizes, in the launch configuration the bench uses."""
+    wl = make(CONFIGS[cfg])
+    print(f"[gpu] full-size config {cfg}", flush=True)
+    out, lse, plan, used = H.run_gpu(wl)
+    O, L = H.oracle_of(wl)
+    m = H.metrics(out, lse, O, L)
+    print(f"[gpu]   {m}", flush=True)
+    H.assert_parity(m, ctx=f"config {cfg}")
+    want = H.plan_words(wl, used)
+    assert np.array_equal(plan.view(torch.int32).numpy()[:len(want)], want)
