@@ -1,0 +1,333 @@
+"""Benchmark of MLA decode over a paged latent cache on one MI355X.
+
+One step = mla_decode + mla_combine over one batch of the workload (the plan is built once per
+forward and timed separately). Inputs are seeded synthetic tensors already resident in HBM.
+Each timed step is preceded (outside its events) by a 512 MB fill that evicts the 256 MB
+Infinity Cache, so the decode reads the cache from HBM; a warm back-to-back figure is reported
+separately. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|1|3|4|5|s1|s4] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "MLA decode: query tokens/s, achieved HBM TB/s & MFMA TFLOP/s, % of roofline"
+DECODE_SRC = os.path.join(ROOT, "mla_paged_latent_plan_amd", "csrc", "decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="2")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+    return ap.parse_args()
+
+
+def get_spec(name):
+    from workloads import CONFIGS, SUPPLEMENTARY
+    if name in SUPPLEMENTARY:
+        return SUPPLEMENTARY[name]
+    return CONFIGS[int(name)]
+
+
+def algorithmic(wl):
+    """Algorithmic HBM bytes and MFMA flops of one decode launch (rows each query may see)."""
+    s = wl.spec
+    from workloads.gen import cache_layout
+    row_bytes = cache_layout(s.kv_format, s.d_qk, s.d_rope, s.page_size)["row_bytes"]
+    if s.kv_format == "fp8":
+        row_bytes += 8  # scale slot
+    L = np.maximum(wl.seqlens.astype(np.int64), 0)
+    Sq, H, B = s.q_len, s.num_heads, s.batch
+    kv_rows = 0
+    vis = 0
+    pages = 0
+    idx_bytes = 0
+    for b in range(B):
+        Lb = int(L[b])
+        if s.topk > 0:
+            idx = wl.indices[b].numpy()
+            rows_b = set()
+            for t in range(Sq):
+                ok = idx[t][(idx[t] >= 0) & (idx[t] < Lb)]
+                vis += len(ok)
+                rows_b.update(ok.tolist())
+            kv_rows += len(rows_b)
+            pages += len({r // s.page_size for r in rows_b})
+            idx_bytes += 4 * Sq * s.topk
+        else:
+            lo_union, n_b = Lb, 0
+            for t in range(Sq):
+                pos = Lb - Sq + t
+                hi = min(Lb - 1, pos) if s.causal else Lb - 1
+                lo = max(0, pos - s.window + 1) if s.window > 0 else 0
+                if hi >= lo:
+                    vis += hi - lo + 1
+                    lo_union = min(lo_union, lo)
+            n_b = Lb - lo_union if Lb > 0 else 0
+            kv_rows += n_b
+            if n_b:
+                pages += (Lb - 1) // s.page_size - lo_union // s.page_size + 1
+    q_bytes = B * Sq * H * s.d_qk * 2
+    o_bytes = B * Sq * H * s.d_v * 2
+    lse_bytes = B * Sq * H * 4
+    total = kv_rows * row_bytes + q_bytes + o_bytes + lse_bytes + 4 * pages + idx_bytes
+    flops = 2.0 * vis * H * (s.d_qk + s.d_v)
+    return dict(bytes=int(total), kv_bytes=int(kv_rows * row_bytes), flops=flops,
+                kv_rows=int(kv_rows), visible_pairs=int(vis))
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.dirname(DECODE_SRC))):
+        with open(os.path.join(os.path.dirname(DECODE_SRC), f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per decode launch from committed counter runs, if the kernels are unchanged."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return int(t["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle, as it stands, on the first requests of the same workload."""
+    import torch
+    from oracle import attention as oatt
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    s = wl.spec
+
+    def run(reqs):
+        q = wl.q[reqs].to(torch.float64).numpy()
+        seq = wl.seqlens[reqs]
+        if s.topk > 0:
+            idx = wl.indices[reqs].numpy()
+
+            class Rows:  # rows are decoded when the oracle indexes them
+                def __init__(self, b):
+                    self.off = int(wl.row_offsets[b])
+
+                def __getitem__(self, J):
+                    J = torch.from_numpy(np.asarray(J, dtype=np.int64) + self.off)
+                    return wl.rows_bf16[J].to(torch.float64).numpy()
+            return oatt.mla_decode(q, lambda i: Rows(reqs[i]), seq, s.sm_scale, s.d_v,
+                                   indices=idx)
+
+        def rows(i):
+            r = wl.request_rows(reqs[i])
+            if s.kv_format == "bf16":
+                return r.to(torch.float64).numpy()
+            from oracle import fp8 as ofp8
+            nope, sc, rope = r
+            return ofp8.dequant_rows(nope.numpy(), sc.numpy(), rope.to(torch.float64).numpy())
+        sink = None if wl.sink is None else wl.sink.to(torch.float64).numpy()
+        return oatt.mla_decode(q, rows, seq, s.sm_scale, s.d_v, s.causal, s.window, sink=sink)
+
+    t0 = time.perf_counter()
+    run([0])
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(s.batch, target_s / max(t1, 1e-3))))
+    reqs = list(range(n))
+    # whole passes over the sample until the time target is reached (at most 10 passes)
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        run(reqs)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s or passes >= 10:
+            break
+    return dict(value=passes * n * s.q_len / dt, unit="query tokens/s", cores=int(threads),
+                kind="oracle",
+                sample=f"{passes} pass(es) over the first {n} of {s.batch} requests of the same "
+                       f"workload, float64 numpy oracle, {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, "
+              "'How the path would shard'); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mla_paged_latent_plan_amd as mla
+    from workloads import make
+
+    spec = get_spec(args.config)
+    wl = make(spec)
+    dev = torch.device("cuda:0")
+    s = spec
+    p = mla.make_problem(s.batch, s.q_len, s.num_heads, s.d_qk,
+                         mla.MLA_KV_BF16 if s.kv_format == "bf16" else mla.MLA_KV_FP8,
+                         s.page_size, wl.page_stride, wl.num_pages, int(wl.block_table.shape[1]),
+                         s.topk, s.causal, s.window)
+    num_cus = s.plan_cus or mla.device_num_cus()
+    runner = mla.MLADecode(p, num_cus, device=dev)
+    q = wl.q.to(dev)
+    cache = wl.cache.to(dev)
+    bt = wl.block_table.to(dev)
+    seq = torch.from_numpy(wl.seqlens).to(dev)
+    idx = None if wl.indices is None else wl.indices.to(dev)
+    sink = None if wl.sink is None else wl.sink.to(dev)
+    out = torch.empty(s.batch, s.q_len, s.num_heads, s.d_v, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(s.batch, s.num_heads, s.q_len, dtype=torch.float32, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def plan():
+        mla.mla_decode_plan(p, num_cus, seq, None if wl.topk_lens is None else
+                            wl.topk_lens.to(dev), runner.plan, stream)
+
+    def decode():
+        mla.mla_decode(p, num_cus, q, cache, bt, seq, s.sm_scale, idx, sink, runner.plan,
+                       runner.partials, out, lse, stream)
+
+    def combine():
+        mla.mla_combine(p, num_cus, runner.plan, runner.partials, sink, out, lse, stream)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # plan (once per forward; timed on its own)
+    plan()
+    torch.cuda.synchronize()
+    pe = [(ev(), ev()) for _ in range(10)]
+    for a, b in pe:
+        a.record(stream)
+        plan()
+        b.record(stream)
+    torch.cuda.synchronize()
+    plan_ms = float(np.median([a.elapsed_time(b) for a, b in pe]))
+
+    for _ in range(args.warmup):
+        decode()
+        combine()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(ev(), ev(), ev()) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        if not args.no_flush:
+            flush.fill_(k & 0xFF)
+        a, m, e = evs[k]
+        a.record(stream)
+        decode()
+        m.record(stream)
+        combine()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / K * 1e3
+    dec_ms = np.array([a.elapsed_time(m) for a, m, _ in evs])
+    com_ms = np.array([m.elapsed_time(e) for _, m, e in evs])
+    step_ms = dec_ms + com_ms
+
+    # warm back-to-back (cache-resident) for context
+    wa, wb = ev(), ev()
+    wa.record(stream)
+    for _ in range(K):
+        decode()
+        combine()
+    wb.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = wa.elapsed_time(wb) / K
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    alg = algorithmic(wl)
+    dec_s = float(dec_ms.mean()) / 1e3
+    ms = float(step_ms.mean())
+    tokens = s.batch * s.q_len
+    achieved_gbs = alg["bytes"] / dec_s / 1e9
+    achieved_tfs = alg["flops"] / dec_s / 1e12
+    ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "hbm" if alg["flops"] / alg["bytes"] < ridge else "mfma"
+    traffic = measured_traffic(s.name)
+    if bound == "hbm":
+        roof = dict(bound="hbm", achieved=round(achieved_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved_gbs / HBM_PEAK_GBS, 4), traffic=traffic)
+    else:
+        roof = dict(bound="mfma", achieved=round(achieved_tfs, 2), peak=MFMA_BF16_PEAK_TFS,
+                    unit="TFLOP/s", frac=round(achieved_tfs / MFMA_BF16_PEAK_TFS, 4),
+                    traffic=traffic)
+    res = {
+        "metric": METRIC,
+        "value": round(tokens / (ms / 1e3), 1),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.kv_format if s.kv_format == "bf16" else "fp8-e4m3/bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{s.name}: batch {s.batch}, q_len {s.q_len}, {s.num_heads} heads, "
+                        f"d_qk {s.d_qk}/d_v {s.d_v} {s.kv_format} rows, page {s.page_size}, "
+                        + (f"lengths U[{s.len_range[0]},{s.len_range[1]}]" if s.len_range
+                           else f"lengths {list(s.seqlens)[:4]}")
+                        + (f", causal" if s.causal else "") + (f", window {s.window}" if s.window else "")
+                        + (f", sink" if s.sink else "") + (f", top-k {s.topk}" if s.topk else ""),
+            "global_batch": s.batch, "seq_len": int(wl.seqlens.max()), "parallelism": "single-gpu",
+            "num_cus_planned": num_cus,
+        },
+        "roofline": roof,
+        "hbm_tbs": round(achieved_gbs / 1e3, 3),
+        "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+        "mfma_tflops": round(achieved_tfs, 2),
+        "mfma_frac": round(achieved_tfs / MFMA_BF16_PEAK_TFS, 4),
+        "decode_ms": round(float(dec_ms.mean()), 4),
+        "decode_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 4),
+                              round(float(np.percentile(dec_ms, 90)), 4)],
+        "combine_ms": round(float(com_ms.mean()), 4),
+        "plan_ms": round(plan_ms, 4),
+        "warm_ms_per_step": round(warm_ms, 4),
+        "wall_ms_per_step_with_flush": round(wall, 4),
+        "algorithmic_bytes": alg["bytes"],
+        "algorithmic_flops": alg["flops"],
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
