@@ -36,7 +36,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
-constexpr int kRowStrideA = 1040;            // latent part: 1 KB + 16 B padding
+constexpr int kRowStrideA = 1056;            // latent part: 1 KB + 32 B padding (bank spread)
 constexpr int kStageA = kBlockRows * kRowStrideA;
 constexpr int kStageB = kBlockRows * 128;    // RoPE tails (64 bf16), XOR-swizzled
 constexpr float kNegInf = -__builtin_inff();
@@ -62,10 +62,10 @@ struct Cfg {
                 "merge scratch must fit in the stage buffers");
 };
 
-// S^T tile row m (MFMA lane index) -> LDS row within the 16-row tile.
-__device__ __forceinline__ int rho(int m) {
-  return 2 * (4 * ((m >> 2) & 1) + (m & 3)) + (m >> 3);
-}
+// S^T tile row m (MFMA lane index) -> LDS row within the 16-row tile. With the 1056-byte row
+// stride the identity order keeps both the K-operand reads and the transposed V reads free of
+// bank conflicts.
+__device__ __forceinline__ int rho(int m) { return m; }
 __device__ __forceinline__ int swz_b(int row) { return (row >> 1) & 7; }
 
 typedef LDS_AS uint8_t* lds_ptr;
@@ -73,8 +73,14 @@ typedef LDS_AS uint8_t* lds_ptr;
 __device__ __forceinline__ bf16x8 lds_read_b128(lds_ptr base, uint32_t off) {
   return *reinterpret_cast<const LDS_AS bf16x8*>(base + off);
 }
+// The restrict-qualified inlined helper gives the transposed read alias metadata. Without it the
+// compiler's wait-count pass cannot tell the read from in-flight LDS-DMA writes and drains every
+// outstanding global load before it; the kernels order DMA and reads with explicit waits instead.
+__device__ __forceinline__ bf16x4 lds_read_tr_nz(LDS_AS bf16x4* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
+}
 __device__ __forceinline__ bf16x4 lds_read_tr(lds_ptr base, uint32_t off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<LDS_AS bf16x4*>(base + off));
+  return lds_read_tr_nz(reinterpret_cast<LDS_AS bf16x4*>(base + off));
 }
 
 __device__ __forceinline__ float wave_max_groups(float v) {
@@ -115,7 +121,7 @@ struct Decoder {
 
   __device__ Decoder(const DecodeArgs& args, lds_ptr base) : a(args), sm(base) {
     lane = threadIdx.x & 63;
-    wave = threadIdx.x >> 6;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
     wm = wave / C::WN;
     wn = wave % C::WN;
   }
@@ -560,6 +566,459 @@ struct Decoder {
   }
 };
 
+// Workgroup barrier for LDS hand-offs only: unlike __syncthreads() it does not wait for
+// outstanding global loads, so the next block's LDS-DMA stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// MFMAs with pinned register classes. The compiler keeps accumulators of builtin MFMAs in AGPRs
+// but loop-carried values in VGPRs, copying every accumulator once per iteration; pinning S^T to
+// VGPRs ("v") and O^T to AGPRs ("a") removes those copies. The hazard recogniser does not see
+// inside inline asm, so every VALU read of their results goes through mfma_drain first.
+__device__ __forceinline__ void mfma_s(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s0(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_o(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// 19 wait states: more than an XDL write -> VALU read of a 16x16x32 MFMA result needs.
+__device__ __forceinline__ void mfma_drain4(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& c3) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
+}
+// Final MFMA of two accumulator chains followed by the wait states, in one statement so that no
+// compiler copy of either result can be scheduled before the results are written.
+__device__ __forceinline__ void mfma_s_last2(f32x4& c0, f32x4& c1, const bf16x8& a0,
+                                             const bf16x8& a1, const bf16x8& b) {
+  asm volatile(
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %4, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %4, %1\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 2"
+      : "+v"(c0), "+v"(c1)
+      : "v"(a0), "v"(a1), "v"(b));
+}
+template <int N>
+__device__ __forceinline__ void mfma_drain_acc(f32x4 (&o)[N][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    asm volatile("" : "+a"(o[i][0]), "+a"(o[i][1]), "+a"(o[i][2]), "+a"(o[i][3]));
+}
+
+// 64 query rows per workgroup, PV split by output columns. Wave w runs QK^T and the softmax of
+// rows [16w, 16w + 16) of the tile, hands P^T to the other waves through LDS, then accumulates O^T
+// for output columns [128w, 128w + 128) of all 64 rows: every wave reads the whole K tile but only
+// a quarter of V, and keeps 72 registers of Q^T and 128 of O^T.
+//
+// KV rows stream through a ring of four 32-row LDS slots, three in flight while one is consumed.
+// Step x's bundle, issued while step x - 3 is consumed, holds the LDS-DMA of step x's rows
+// (zero-row reads past the split's end), the block-table entries of step x + 3 and, with index
+// lists, the index entries of step x + 6. Block-table and index entries also travel by LDS-DMA,
+// into small per-wave rings, so no register waits on an in-flight load; their addresses are
+// clamped and the values validated when consumed. Every bundle therefore holds the same number
+// of memory operations, and "bundle x has landed" is an exact vmcnt.
+template <int DQK>
+struct Col64 {
+  static constexpr bool HAS_B = DQK > 512;
+  static constexpr int KS = DQK / 32;
+  static constexpr int kRows = 32;                         // rows per slot / step
+  static constexpr int kSlotA = kRows * kRowStrideA;
+  static constexpr int kSlot = kSlotA + (HAS_B ? kRows * 128 : 0);
+  static constexpr uint32_t kPOff = 4 * kSlot;             // P^T fragments [4 row tiles][64]
+  static constexpr uint32_t kAOff = kPOff + 4 * 1024;      // rescale factors [64]
+  static constexpr uint32_t kFOff = kAOff + 256;           // per-wave rescale flags [4]
+  static constexpr uint32_t kLOff = kFOff + 16;            // final l [64], then m [64]
+  static constexpr uint32_t kRiOff = kLOff + 512;          // per-wave rings of row entries:
+  static constexpr int kRiWave = 4 * 128 + 8 * 128;        //   block-table [4][32], index [8][32]
+  static constexpr int LDS = kRiOff + 4 * kRiWave;
+  static constexpr int kDmaOps = 8 + (HAS_B ? 1 : 0);     // LDS-DMA instructions per wave per slot
+
+  const DecodeArgs& a;
+  lds_ptr sm;
+  int lane, wave, rl;
+  int g, b, L, j0, n;
+
+  __device__ Col64(const DecodeArgs& args, lds_ptr base) : a(args), sm(base) {
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    rl = lane & 31;  // row of a step that this lane describes (lanes 32..63 mirror 0..31)
+  }
+
+  // --- row description pipeline ------------------------------------------------------------
+  // Step x covers effective rows [32 x, 32 x + 32) of the group; lane rl describes row 32 x + rl.
+  __device__ __forceinline__ uint32_t pg_slot(int x) const { return kRiOff + wave * kRiWave + (x & 3) * 128; }
+  __device__ __forceinline__ uint32_t ix_slot(int x) const {
+    return kRiOff + wave * kRiWave + 512 + (x & 7) * 128;
+  }
+  __device__ __forceinline__ void dma_dword(const int32_t* src, uint32_t dst) const {
+    if (lane < 32)
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + dst), 4, 0, 0);
+  }
+  __device__ __forceinline__ int ri_read(uint32_t slot) const {
+    return *reinterpret_cast<const LDS_AS int*>(sm + slot + 4 * rl);
+  }
+  // index entries of step x (clamped address)
+  __device__ __forceinline__ void idx_fetch(int x) const {
+    const int k = min(32 * x + rl, a.topk - 1);
+    dma_dword(a.indices + (int64_t)g * a.topk + max(k, 0), ix_slot(x));
+  }
+  // logical position of row 32 x + rl (index entries of step x must have landed)
+  __device__ __forceinline__ int row_j(int x) const {
+    return (a.topk > 0) ? ri_read(ix_slot(x)) : j0 + 32 * x + rl;
+  }
+  // block-table entries of step x (clamped address)
+  __device__ __forceinline__ void page_fetch(int x) const {
+    const int j = row_j(x);
+    const int pi = min(max(j >> a.ps_log2, 0), a.max_pages - 1);
+    dma_dword(a.block_table + (int64_t)b * a.max_pages + pi, pg_slot(x));
+  }
+  __device__ __forceinline__ bool row_ok(int x, int j) const {
+    const int k = 32 * x + rl;
+    bool ok = k < n;
+    if (a.topk > 0) ok = ok && j >= 0 && j < L;
+    return ok && (j >> a.ps_log2) < a.max_pages;
+  }
+  __device__ __forceinline__ uint64_t row_base(int j, bool ok, int page, bool* valid) const {
+    ok = ok && page >= 0 && (int64_t)page < a.num_pages;
+    *valid = ok;
+    if (!ok) return (uint64_t)(uintptr_t)a.zero_row;
+    const int slot = j & ((1 << a.ps_log2) - 1);
+    return (uint64_t)(uintptr_t)(a.cache + (int64_t)page * a.page_stride + (int64_t)slot * a.row_bytes);
+  }
+
+  // LDS-DMA of one 32-row step into slot `sl`; lane rl < 32 holds the address of row rl.
+  __device__ __forceinline__ void issue(int sl, uint64_t base) const {
+    const uint32_t sa = sl * kSlot;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wave * 8 + i;
+      const uint64_t rb = readlane64(base, r);
+      const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 16 * lane;
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + r * kRowStrideA),
+                                       16, 0, 0);
+    }
+    if constexpr (HAS_B) {
+      const int r = wave * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz_b(r);
+      const uint32_t lo = __shfl((uint32_t)base, r, 64);
+      const uint32_t hi = __shfl((uint32_t)(base >> 32), r, 64);
+      const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo)) +
+                           1024 + 16 * c;
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + kSlotA + wave * 1024),
+                                       16, 0, 0);
+    }
+  }
+
+  __device__ void run_split(int s, int mt) {
+    const int32_t* plan = a.plan;
+    const int32_t* rec = plan + a.splits_off + 4 * (int64_t)s;
+    g = rec[0];
+    const int kb = rec[1], ke = rec[2];
+    j0 = plan[a.grp_rows_off + 2 * g];
+    n = plan[a.grp_rows_off + 2 * g + 1];
+    const int nsplit = plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g];
+    b = (a.topk > 0) ? g / a.Sq : g;
+    L = a.seqlens[b];
+    const int nl = lane & 15, gl = lane >> 4;
+    const int tile0 = mt * 64;
+    const int qrow = tile0 + wave * 16 + nl;  // this lane's softmax row
+    const int q0 = 2 * kb;
+    const int qend = min(2 * ke, (n + kRows - 1) / kRows);  // steps holding at least one row
+
+    // Q^T of the wave's 16 rows (rows past R repeat the last row; their outputs are dropped)
+    bf16x8 qr[KS];
+    {
+      const int r = min(qrow, a.R - 1);
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(a.q + ((int64_t)g * a.R + r) * DQK + 8 * gl);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qr[ks] = src[4 * ks];
+    }
+    const int qpos = L - a.Sq + ((a.topk > 0) ? 0 : (qrow / a.H));
+    float m_ref = kNegInf, l_acc = 0.f;
+    f32x4 o[8][4];  // [output column tile of this wave][row tile]
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- prologue: row entries of the first steps, then three bundles in flight --------------
+    const bool sparse = a.topk > 0;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // LDS rings free
+    if (sparse) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) idx_fetch(q0 + i);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) page_fetch(q0 + i);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // bundle x: rows of step x (entries landed), block-table entries of x + 3, index entries of x + 6
+    auto bundle = [&](int x) -> uint32_t {
+      const int j = row_j(x);
+      const int page = ri_read(pg_slot(x));
+      bool v;
+      const uint64_t base = row_base(j, x < qend && row_ok(x, j), page, &v);
+      const uint32_t m = (uint32_t)__ballot(v);
+      issue(x & 3, base);
+      page_fetch(x + 3);
+      if (sparse) idx_fetch(x + 6);
+      return m;
+    };
+    uint32_t vm[3];  // row-valid masks of the steps in flight
+    vm[0] = bundle(q0);
+    vm[1] = bundle(q0 + 1);
+    vm[2] = bundle(q0 + 2);
+    const bool dense_mask = (a.topk == 0) && (a.causal || a.window > 0);
+
+    for (int q = q0; q < qend; ++q) {
+      const int sl = q & 3;
+      const uint32_t vmask = vm[0];
+      // bundle q landed, bundles q + 1 and q + 2 may still be in flight
+      if (sparse) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * (kDmaOps + 2)) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * (kDmaOps + 1)) : "memory");
+      lds_barrier();  // every wave's rows of step q landed; slot q - 1 is free for bundle q + 3
+      vm[0] = vm[1];
+      vm[1] = vm[2];
+      vm[2] = bundle(q + 3);
+      const uint32_t sa = sl * kSlot;
+      const uint32_t sb = sa + kSlotA;
+
+      // ---- S^T = K Q^T: 32 step rows x this wave's 16 rows ---------------------------------
+      uint32_t kaddr[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) kaddr[kt] = sa + (16 * kt + nl) * kRowStrideA + 16 * gl;
+      auto k_operand = [&](int kt, int ks) -> bf16x8 {
+        if (ks < 16) return lds_read_b128(sm, kaddr[kt] + 64 * ks);
+        const int row = 16 * kt + nl;
+        const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
+        return lds_read_b128(sm, sb + row * 128 + 16 * c);
+      };
+      constexpr int D = 4;  // operand steps in flight
+      bf16x8 ka[D][2];
+#pragma unroll
+      for (int i = 0; i < D - 1; ++i)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) ka[i][kt] = k_operand(kt, i);
+      f32x4 sacc[2];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + D - 1 < KS) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) ka[(ks + D - 1) % D][kt] = k_operand(kt, ks + D - 1);
+        }
+        if (ks == KS - 1) {
+          mfma_s_last2(sacc[0], sacc[1], ka[ks % D][0], ka[ks % D][1], qr[ks]);
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            if (ks == 0) mfma_s0(sacc[kt], ka[0][kt], qr[0]);
+            else mfma_s(sacc[kt], ka[ks % D][kt], qr[ks]);
+          }
+        }
+      }
+
+      // ---- masks -----------------------------------------------------------------------------
+      const bool tail = 32 * (q + 1) > n;
+      bool need_mask = tail || dense_mask;
+      if (sparse) need_mask = (vmask != ~0u);
+      if (need_mask) {
+        const int causal_hi = a.causal ? 0 : (1 << 30);
+        const int win = a.window > 0 ? a.window : (1 << 30);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * kt + 4 * gl + e;
+            const int k = 32 * q + row;
+            const int j = j0 + k;
+            const bool ok = sparse ? (((vmask >> row) & 1u) != 0)
+                                   : (k < n && j <= qpos + causal_hi && j >= qpos - win + 1);
+            sacc[kt][e] = ok ? sacc[kt][e] : kNegInf;
+          }
+      }
+
+      // ---- softmax of this wave's rows (base 2, lazy reference maximum) ----------------------
+      float mx = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kt][e]);
+      mx = wave_max_groups(mx);
+      const float mnew = mx * a.scale_log2;  // -inf stays -inf (scale > 0)
+      const bool up = mnew > m_ref + kTau;
+      float alpha = 1.f;
+      if (up) {
+        alpha = __builtin_amdgcn_exp2f(m_ref - mnew);  // m_ref = -inf -> 0
+        m_ref = mnew;
+        l_acc *= alpha;
+      }
+      const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
+      bf16x8 pf;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], a.scale_log2, -mu));
+          lsum += pv;
+          pf[kt * 4 + e] = (__bf16)pv;
+        }
+      l_acc += lsum;
+      const bool wave_up = __any(up);
+      lds_barrier();  // PV of the previous step has read the P^T / factor buffers
+      *reinterpret_cast<LDS_AS bf16x8*>(sm + kPOff + (wave * 64 + lane) * 16) = pf;
+      if (gl == 0) *reinterpret_cast<LDS_AS float*>(sm + kAOff + 4 * (16 * wave + nl)) = alpha;
+      if (lane == 0) *reinterpret_cast<LDS_AS int*>(sm + kFOff + 4 * wave) = wave_up ? 1 : 0;
+      lds_barrier();
+
+      // ---- O^T[128 w .. 128 w + 127][64 rows] += V^T P^T -------------------------------------
+      {
+        const LDS_AS int* fl = reinterpret_cast<const LDS_AS int*>(sm + kFOff);
+        if (fl[0] | fl[1] | fl[2] | fl[3]) {
+          mfma_drain_acc(o);
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) {
+            const float al = *reinterpret_cast<const LDS_AS float*>(sm + kAOff + 4 * (16 * ht + nl));
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+              o[dt][ht] *= al;
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+      }
+      bf16x8 pb[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+        pb[ht] = *reinterpret_cast<const LDS_AS bf16x8*>(sm + kPOff + (ht * 64 + lane) * 16);
+      const uint32_t vbase = sa + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (lane & 3) + 256 * wave;
+      auto v_operand = [&](int dt) -> bf16x8 {
+        const uint32_t ad = vbase + 32 * dt;
+        const bf16x4 v0 = lds_read_tr(sm, ad);
+        const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 va[3];
+      va[0] = v_operand(0);
+      va[1] = v_operand(1);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        if (dt + 2 < 8) va[(dt + 2) % 3] = v_operand(dt + 2);
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) mfma_o(o[dt][ht], va[dt % 3], pb[ht]);
+      }
+    }
+    // the last bundles (zero-row reads) must land before the slots are reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    mfma_drain_acc(o);
+
+    // ---- epilogue: row statistics to every wave, then each wave writes its columns ----------
+    {
+      const float lt = wave_sum_groups(l_acc);
+      if (gl == 0) {
+        *reinterpret_cast<LDS_AS float*>(sm + kLOff + 4 * (wave * 16 + nl)) = lt;
+        *reinterpret_cast<LDS_AS float*>(sm + kLOff + 256 + 4 * (wave * 16 + nl)) = m_ref;
+      }
+    }
+    __syncthreads();
+    const bool final_out = (nsplit == 1);
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const int hrow = ht * 16 + nl;
+      const int r = tile0 + hrow;
+      const float lt = *reinterpret_cast<const LDS_AS float*>(sm + kLOff + 4 * hrow);
+      const float m2 = *reinterpret_cast<const LDS_AS float*>(sm + kLOff + 256 + 4 * hrow);
+      if (r < a.R) {
+        float lse_nat, scale;
+        row_norm(r, m2, lt, final_out, &lse_nat, &scale);
+        const int col0 = 128 * wave + 4 * gl;
+        if (final_out) {
+          uint16_t* dst = a.out + ((int64_t)g * a.R + r) * kDv + col0;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            const f32x4 v = o[dt][ht] * scale;
+            uint2 w;
+            w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+            w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+            *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (wave == 0 && gl == 0) a.lse[lse_index(r)] = lse_nat;
+        } else {
+          float* dst = a.part_o + ((int64_t)s * a.R + r) * kDv + col0;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt][ht] * scale;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (wave == 0 && gl == 0) a.part_lse[(int64_t)s * a.R + r] = lse_nat;
+        }
+      }
+    }
+    __syncthreads();  // statistics buffer and slots reused by the next split
+  }
+
+  // LSE (natural log) and output scale of a row; the sink is folded in for final outputs.
+  __device__ __forceinline__ void row_norm(int r, float m2, float l, bool final_out, float* lse_nat,
+                                           float* scale) const {
+    const float kLn2 = 0.69314718055994530942f;
+    if (l > 0.f) {
+      float lse = (m2 + __log2f(l)) * kLn2;
+      float sc = 1.f / l;
+      if (final_out && a.sink != nullptr) {
+        const float sk = a.sink[(a.topk > 0) ? r : r % a.H];
+        const float mx = fmaxf(lse, sk);
+        const float lse2 = mx + __logf(__expf(lse - mx) + __expf(sk - mx));
+        sc *= __expf(lse - lse2);
+        lse = lse2;
+      }
+      *lse_nat = lse;
+      *scale = sc;
+    } else {
+      *scale = 0.f;
+      *lse_nat = (final_out && a.sink != nullptr) ? a.sink[(a.topk > 0) ? r : r % a.H] : kNegInf;
+    }
+  }
+  __device__ __forceinline__ int64_t lse_index(int r) const {
+    int bb, t, h;
+    if (a.topk > 0) {
+      bb = g / a.Sq;
+      t = g % a.Sq;
+      h = r;
+    } else {
+      bb = g;
+      t = r / a.H;
+      h = r % a.H;
+    }
+    return ((int64_t)bb * a.H + h) * a.Sq + t;
+  }
+};
+
+// Workgroup b -> (unit, row tile): all row tiles of a unit land on the same XCD (workgroups are
+// dealt to the 8 XCDs round-robin), so the second reader of a KV block finds it in that L2.
+__device__ __forceinline__ void unit_tile(int bid, int m_tiles, int* unit, int* mt) {
+  const int x = bid & 7, q = bid >> 3;
+  *mt = q % m_tiles;
+  *unit = (q / m_tiles) * 8 + x;
+}
+
+template <int DQK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_col64_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Col64<DQK>::LDS];
+  const lds_ptr base = (lds_ptr)lds;
+  int unit, mt;
+  unit_tile(blockIdx.x, a.m_tiles, &unit, &mt);
+  if (unit >= a.U) return;
+  const int s0 = a.plan[a.unit_ptr_off + unit];
+  const int s1 = a.plan[a.unit_ptr_off + unit + 1];
+  Col64<DQK> d(a, base);
+  for (int s = s0; s < s1; ++s) d.run_split(s, mt);
+}
+
 template <class C>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(DecodeArgs a) {
@@ -587,10 +1046,19 @@ hipError_t launch_cfg(DecodeArgs a, hipStream_t s) {
 }
 
 template <int DQK>
+hipError_t launch_col64(DecodeArgs a, hipStream_t s) {
+  a.m_tiles = (a.R + 63) / 64;
+  const int64_t grid = (int64_t)((a.U + 7) / 8) * 8 * a.m_tiles;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_col64_kernel<DQK>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DQK>
 hipError_t launch_dqk(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
   if (sh.R <= 16) return launch_cfg<Cfg<16, 4, DQK>>(a, s);
   if (sh.R <= 32) return launch_cfg<Cfg<16, 2, DQK>>(a, s);
-  return launch_cfg<Cfg<16, 1, DQK>>(a, s);
+  return launch_col64<DQK>(a, s);
 }
 
 }  // namespace

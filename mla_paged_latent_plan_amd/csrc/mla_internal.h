@@ -42,8 +42,7 @@ struct PlanLayout {
 inline void tile_params(int R, int* m_tile, int* fixed) {
   if (R <= 16) { *m_tile = 16; *fixed = 1; }
   else if (R <= 32) { *m_tile = 32; *fixed = 2; }
-  else if (R <= 64) { *m_tile = 64; *fixed = 2; }
-  else { *m_tile = 128; *fixed = 4; }
+  else { *m_tile = 64; *fixed = 2; }
 }
 
 struct Shape {  // derived, validated problem shape
