@@ -589,16 +589,21 @@ __device__ __forceinline__ void mfma_o(f32x4& c, const bf16x8& a, const bf16x8& 
 __device__ __forceinline__ void mfma_drain4(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& c3) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
 }
-// Final MFMA of two accumulator chains followed by the wait states, in one statement so that no
-// compiler copy of either result can be scheduled before the results are written.
-__device__ __forceinline__ void mfma_s_last2(f32x4& c0, f32x4& c1, const bf16x8& a0,
-                                             const bf16x8& a1, const bf16x8& b) {
+// Score MFMAs with the Q^T operand held in accumulation registers.
+__device__ __forceinline__ void mfma_sq(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_sq0(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_sq_last2(f32x4& c0, f32x4& c1, const bf16x8& a0,
+                                              const bf16x8& a1, const bf16x8& b) {
   asm volatile(
       "v_mfma_f32_16x16x32_bf16 %0, %2, %4, %0\n\t"
       "v_mfma_f32_16x16x32_bf16 %1, %3, %4, %1\n\t"
       "s_nop 7\n\ts_nop 7\n\ts_nop 2"
       : "+v"(c0), "+v"(c1)
-      : "v"(a0), "v"(a1), "v"(b));
+      : "v"(a0), "v"(a1), "a"(b));
 }
 template <int N>
 __device__ __forceinline__ void mfma_drain_acc(f32x4 (&o)[N][4]) {
@@ -608,145 +613,272 @@ __device__ __forceinline__ void mfma_drain_acc(f32x4 (&o)[N][4]) {
     asm volatile("" : "+a"(o[i][0]), "+a"(o[i][1]), "+a"(o[i][2]), "+a"(o[i][3]));
 }
 
-// 64 query rows per workgroup, PV split by output columns. Wave w runs QK^T and the softmax of
-// rows [16w, 16w + 16) of the tile, hands P^T to the other waves through LDS, then accumulates O^T
-// for output columns [128w, 128w + 128) of all 64 rows: every wave reads the whole K tile but only
-// a quarter of V, and keeps 72 registers of Q^T and 128 of O^T.
+// 64 query rows per workgroup, eight waves in two roles, two waves per SIMD:
+//  * score waves 0-3: QK^T and the softmax of rows [16w, 16w + 16) of the tile (Q^T held in
+//    accumulation registers), P^T handed to the value waves through a double-buffered LDS tile;
+//  * value waves 4-7: O^T for output columns [128v, 128v + 128) of all 64 rows, plus every
+//    global -> LDS transfer.
+// In step t the score waves work on KV step t while the value waves accumulate step t - 1, so each
+// SIMD interleaves one wave's MFMAs with the other's softmax, LDS waits and DMA issue. One
+// workgroup barrier per step hands P^T over and recycles KV slots.
 //
-// KV rows stream through a ring of four 32-row LDS slots, three in flight while one is consumed.
-// Step x's bundle, issued while step x - 3 is consumed, holds the LDS-DMA of step x's rows
-// (zero-row reads past the split's end), the block-table entries of step x + 3 and, with index
-// lists, the index entries of step x + 6. Block-table and index entries also travel by LDS-DMA,
-// into small per-wave rings, so no register waits on an in-flight load; their addresses are
-// clamped and the values validated when consumed. Every bundle therefore holds the same number
-// of memory operations, and "bundle x has landed" is an exact vmcnt.
+// KV rows stream through a ring of four 32-row LDS slots (K of step t and V of step t - 1 being
+// read, steps t + 1 and t + 2 in flight). Value wave v moves rows [8v, 8v + 8) of every step. Step
+// x's bundle, issued at the start of step x - 2, holds the LDS-DMA of step x's rows (zero-row reads
+// past the split's end), the block-table entries of step x + 3 and, with index lists, the index
+// entries of step x + 6. Block-table and index entries travel by LDS-DMA into small per-wave rings,
+// so no register waits on an in-flight load; their addresses are clamped and the values validated
+// when consumed. Every bundle holds the same number of memory operations, so "bundle x has landed"
+// is an exact vmcnt.
 template <int DQK>
-struct Col64 {
+struct Spec64 {
   static constexpr bool HAS_B = DQK > 512;
   static constexpr int KS = DQK / 32;
   static constexpr int kRows = 32;                         // rows per slot / step
   static constexpr int kSlotA = kRows * kRowStrideA;
   static constexpr int kSlot = kSlotA + (HAS_B ? kRows * 128 : 0);
-  static constexpr uint32_t kPOff = 4 * kSlot;             // P^T fragments [4 row tiles][64]
-  static constexpr uint32_t kAOff = kPOff + 4 * 1024;      // rescale factors [64]
-  static constexpr uint32_t kFOff = kAOff + 256;           // per-wave rescale flags [4]
-  static constexpr uint32_t kLOff = kFOff + 16;            // final l [64], then m [64]
-  static constexpr uint32_t kRiOff = kLOff + 512;          // per-wave rings of row entries:
-  static constexpr int kRiWave = 4 * 128 + 8 * 128;        //   block-table [4][32], index [8][32]
+  static constexpr uint32_t kPOff = 4 * kSlot;             // P^T fragments [2][4 row tiles][64]
+  static constexpr uint32_t kAOff = kPOff + 2 * 4096;      // rescale factors [2][64]
+  static constexpr uint32_t kFOff = kAOff + 2 * 256;       // rescale flags [2][4]
+  static constexpr uint32_t kMOff = kFOff + 32;            // row-valid masks [4 steps][4 bytes]
+  static constexpr uint32_t kLOff = kMOff + 16;            // final l [64], then m [64]
+  static constexpr uint32_t kRiOff = kLOff + 512;          // per value wave: block-table entries
+  static constexpr int kRiWave = 4 * 32 + 8 * 32;          //   [4][8], index entries [8][8]
   static constexpr int LDS = kRiOff + 4 * kRiWave;
-  static constexpr int kDmaOps = 8 + (HAS_B ? 1 : 0);     // LDS-DMA instructions per wave per slot
+  static constexpr int kDmaOps = 8 + (HAS_B ? 1 : 0);     // row LDS-DMA instructions per bundle
 
   const DecodeArgs& a;
   lds_ptr sm;
-  int lane, wave, rl;
-  int g, b, L, j0, n;
+  int lane, wave;
+  int g, b, L, j0, n, q0, qend, nsplit;
 
-  __device__ Col64(const DecodeArgs& args, lds_ptr base) : a(args), sm(base) {
+  __device__ Spec64(const DecodeArgs& args, lds_ptr base) : a(args), sm(base) {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    rl = lane & 31;  // row of a step that this lane describes (lanes 32..63 mirror 0..31)
   }
 
-  // --- row description pipeline ------------------------------------------------------------
-  // Step x covers effective rows [32 x, 32 x + 32) of the group; lane rl describes row 32 x + rl.
-  __device__ __forceinline__ uint32_t pg_slot(int x) const { return kRiOff + wave * kRiWave + (x & 3) * 128; }
+  // ===== value waves: row description pipeline and DMA =======================================
+  // Value wave v describes rows 8v + (lane & 7) of a step (lanes 8..63 repeat lanes 0..7).
+  __device__ __forceinline__ int vrow() const { return 8 * (wave - 4) + (lane & 7); }
+  __device__ __forceinline__ uint32_t pg_slot(int x) const {
+    return kRiOff + (wave - 4) * kRiWave + (x & 3) * 32;
+  }
   __device__ __forceinline__ uint32_t ix_slot(int x) const {
-    return kRiOff + wave * kRiWave + 512 + (x & 7) * 128;
+    return kRiOff + (wave - 4) * kRiWave + 128 + (x & 7) * 32;
   }
   __device__ __forceinline__ void dma_dword(const int32_t* src, uint32_t dst) const {
-    if (lane < 32)
+    if (lane < 8)
       __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + dst), 4, 0, 0);
   }
   __device__ __forceinline__ int ri_read(uint32_t slot) const {
-    return *reinterpret_cast<const LDS_AS int*>(sm + slot + 4 * rl);
+    return *reinterpret_cast<const LDS_AS int*>(sm + slot + 4 * (lane & 7));
   }
-  // index entries of step x (clamped address)
-  __device__ __forceinline__ void idx_fetch(int x) const {
-    const int k = min(32 * x + rl, a.topk - 1);
+  __device__ __forceinline__ void idx_fetch(int x) const {  // index entries of step x
+    const int k = min(32 * x + vrow(), a.topk - 1);
     dma_dword(a.indices + (int64_t)g * a.topk + max(k, 0), ix_slot(x));
   }
-  // logical position of row 32 x + rl (index entries of step x must have landed)
-  __device__ __forceinline__ int row_j(int x) const {
-    return (a.topk > 0) ? ri_read(ix_slot(x)) : j0 + 32 * x + rl;
+  __device__ __forceinline__ int row_j(int x) const {  // logical position of the row
+    return (a.topk > 0) ? ri_read(ix_slot(x)) : j0 + 32 * x + vrow();
   }
-  // block-table entries of step x (clamped address)
-  __device__ __forceinline__ void page_fetch(int x) const {
+  __device__ __forceinline__ void page_fetch(int x) const {  // block-table entries of step x
     const int j = row_j(x);
     const int pi = min(max(j >> a.ps_log2, 0), a.max_pages - 1);
     dma_dword(a.block_table + (int64_t)b * a.max_pages + pi, pg_slot(x));
   }
-  __device__ __forceinline__ bool row_ok(int x, int j) const {
-    const int k = 32 * x + rl;
-    bool ok = k < n;
+  __device__ __forceinline__ uint64_t row_base(int x, bool* valid) const {
+    const int j = row_j(x);
+    const int page = ri_read(pg_slot(x));
+    const int k = 32 * x + vrow();
+    bool ok = x < qend && k < n && (j >> a.ps_log2) < a.max_pages;
     if (a.topk > 0) ok = ok && j >= 0 && j < L;
-    return ok && (j >> a.ps_log2) < a.max_pages;
-  }
-  __device__ __forceinline__ uint64_t row_base(int j, bool ok, int page, bool* valid) const {
     ok = ok && page >= 0 && (int64_t)page < a.num_pages;
     *valid = ok;
     if (!ok) return (uint64_t)(uintptr_t)a.zero_row;
     const int slot = j & ((1 << a.ps_log2) - 1);
     return (uint64_t)(uintptr_t)(a.cache + (int64_t)page * a.page_stride + (int64_t)slot * a.row_bytes);
   }
-
-  // LDS-DMA of one 32-row step into slot `sl`; lane rl < 32 holds the address of row rl.
-  __device__ __forceinline__ void issue(int sl, uint64_t base) const {
-    const uint32_t sa = sl * kSlot;
+  __device__ __forceinline__ void bundle(int x) const {
+    bool v;
+    const uint64_t base = row_base(x, &v);
+    const uint32_t m = (uint32_t)__ballot(v) & 0xFFu;
+    if (lane == 0) *reinterpret_cast<LDS_AS uint8_t*>(sm + kMOff + 4 * (x & 3) + (wave - 4)) = (uint8_t)m;
+    const uint32_t sa = (x & 3) * kSlot;
+    const int r0 = 8 * (wave - 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = wave * 8 + i;
-      const uint64_t rb = readlane64(base, r);
+      const uint64_t rb = readlane64(base, i);
       const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 16 * lane;
-      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + r * kRowStrideA),
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + (r0 + i) * kRowStrideA),
                                        16, 0, 0);
     }
     if constexpr (HAS_B) {
-      const int r = wave * 8 + (lane >> 3);
+      const int r = r0 + (lane >> 3);
       const int c = (lane & 7) ^ swz_b(r);
-      const uint32_t lo = __shfl((uint32_t)base, r, 64);
-      const uint32_t hi = __shfl((uint32_t)(base >> 32), r, 64);
+      const uint32_t lo = __shfl((uint32_t)base, lane >> 3, 64);
+      const uint32_t hi = __shfl((uint32_t)(base >> 32), lane >> 3, 64);
       const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo)) +
                            1024 + 16 * c;
-      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + kSlotA + wave * 1024),
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + kSlotA + (wave - 4) * 1024),
                                        16, 0, 0);
     }
+    page_fetch(x + 3);
+    if (a.topk > 0) idx_fetch(x + 6);
   }
 
-  __device__ void run_split(int s, int mt) {
+  __device__ __forceinline__ void load_split(int s) {
     const int32_t* plan = a.plan;
     const int32_t* rec = plan + a.splits_off + 4 * (int64_t)s;
     g = rec[0];
     const int kb = rec[1], ke = rec[2];
     j0 = plan[a.grp_rows_off + 2 * g];
     n = plan[a.grp_rows_off + 2 * g + 1];
-    const int nsplit = plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g];
+    nsplit = plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g];
     b = (a.topk > 0) ? g / a.Sq : g;
     L = a.seqlens[b];
-    const int nl = lane & 15, gl = lane >> 4;
-    const int tile0 = mt * 64;
-    const int qrow = tile0 + wave * 16 + nl;  // this lane's softmax row
-    const int q0 = 2 * kb;
-    const int qend = min(2 * ke, (n + kRows - 1) / kRows);  // steps holding at least one row
+    q0 = 2 * kb;
+    qend = min(2 * ke, (n + kRows - 1) / kRows);  // steps holding at least one row
+  }
 
-    // Q^T of the wave's 16 rows (rows past R repeat the last row; their outputs are dropped)
+  // ===== score waves ===========================================================================
+  __device__ void score_split(int mt) {
+    const int nl = lane & 15, gl = lane >> 4;
+    const int qrow = mt * 64 + wave * 16 + nl;  // this lane's softmax row
+    // Q^T of the wave's 16 rows (rows past R repeat the last row; their outputs are dropped),
+    // kept in accumulation registers for the whole split
     bf16x8 qr[KS];
     {
       const int r = min(qrow, a.R - 1);
       const bf16x8* src = reinterpret_cast<const bf16x8*>(a.q + ((int64_t)g * a.R + r) * DQK + 8 * gl);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qr[ks] = src[4 * ks];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(qr[ks]));
     }
-    const int qpos = L - a.Sq + ((a.topk > 0) ? 0 : (qrow / a.H));
+    const bool sparse = a.topk > 0;
+    const int qpos = L - a.Sq + (sparse ? 0 : (qrow / a.H));
+    const bool dense_mask = !sparse && (a.causal || a.window > 0);
     float m_ref = kNegInf, l_acc = 0.f;
+    lds_barrier();  // prologue: step q0 landed
+
+    for (int t = q0; t <= qend; ++t) {
+      if (t < qend) {
+        const uint32_t sa = (t & 3) * kSlot;
+        const uint32_t sb = sa + kSlotA;
+        // ---- S^T = K Q^T: 32 step rows x this wave's 16 rows -------------------------------
+        uint32_t kaddr[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) kaddr[kt] = sa + (16 * kt + nl) * kRowStrideA + 16 * gl;
+        auto k_operand = [&](int kt, int ks) -> bf16x8 {
+          if (ks < 16) return lds_read_b128(sm, kaddr[kt] + 64 * ks);
+          const int row = 16 * kt + nl;
+          const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
+          return lds_read_b128(sm, sb + row * 128 + 16 * c);
+        };
+        constexpr int D = 4;  // operand steps in flight
+        bf16x8 ka[D][2];
+#pragma unroll
+        for (int i = 0; i < D - 1; ++i)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) ka[i][kt] = k_operand(kt, i);
+        f32x4 sacc[2];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + D - 1 < KS) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) ka[(ks + D - 1) % D][kt] = k_operand(kt, ks + D - 1);
+          }
+          if (ks == KS - 1) {
+            mfma_sq_last2(sacc[0], sacc[1], ka[ks % D][0], ka[ks % D][1], qr[ks]);
+          } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              if (ks == 0) mfma_sq0(sacc[kt], ka[0][kt], qr[0]);
+              else mfma_sq(sacc[kt], ka[ks % D][kt], qr[ks]);
+            }
+          }
+        }
+
+        // ---- masks ---------------------------------------------------------------------------
+        const bool tail = 32 * (t + 1) > n;
+        const uint32_t vmask = *reinterpret_cast<const LDS_AS uint32_t*>(sm + kMOff + 4 * (t & 3));
+        const bool need_mask = sparse ? (vmask != ~0u) : (tail || dense_mask);
+        if (need_mask) {
+          const int causal_hi = a.causal ? 0 : (1 << 30);
+          const int win = a.window > 0 ? a.window : (1 << 30);
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int row = 16 * kt + 4 * gl + e;
+              const int k = 32 * t + row;
+              const int j = j0 + k;
+              const bool ok = sparse ? (((vmask >> row) & 1u) != 0)
+                                     : (k < n && j <= qpos + causal_hi && j >= qpos - win + 1);
+              sacc[kt][e] = ok ? sacc[kt][e] : kNegInf;
+            }
+        }
+
+        // ---- softmax of this wave's rows (base 2, lazy reference maximum) --------------------
+        float mx = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kt][e]);
+        mx = wave_max_groups(mx);
+        const float mnew = mx * a.scale_log2;  // -inf stays -inf (scale > 0)
+        const bool up = mnew > m_ref + kTau;
+        float alpha = 1.f;
+        if (up) {
+          alpha = __builtin_amdgcn_exp2f(m_ref - mnew);  // m_ref = -inf -> 0
+          m_ref = mnew;
+          l_acc *= alpha;
+        }
+        const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
+        bf16x8 pf;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], a.scale_log2, -mu));
+            lsum += pv;
+            pf[kt * 4 + e] = (__bf16)pv;
+          }
+        l_acc += lsum;
+        const bool wave_up = __any(up);
+        const uint32_t pb = (t & 1);
+        *reinterpret_cast<LDS_AS bf16x8*>(sm + kPOff + pb * 4096 + (wave * 64 + lane) * 16) = pf;
+        if (gl == 0) *reinterpret_cast<LDS_AS float*>(sm + kAOff + pb * 256 + 4 * (16 * wave + nl)) = alpha;
+        if (lane == 0) *reinterpret_cast<LDS_AS int*>(sm + kFOff + pb * 16 + 4 * wave) = wave_up ? 1 : 0;
+      }
+      lds_barrier();  // P^T of step t published; K slot of step t released
+    }
+    // ---- row statistics for the value waves --------------------------------------------------
+    const float lt = wave_sum_groups(l_acc);
+    if (gl == 0) {
+      *reinterpret_cast<LDS_AS float*>(sm + kLOff + 4 * (wave * 16 + nl)) = lt;
+      *reinterpret_cast<LDS_AS float*>(sm + kLOff + 256 + 4 * (wave * 16 + nl)) = m_ref;
+    }
+    lds_barrier();  // statistics published
+    lds_barrier();  // value waves done with the split's LDS
+  }
+
+  // ===== value waves ===========================================================================
+  __device__ void value_split(int s, int mt) {
+    const int vw = wave - 4;
+    const int nl = lane & 15, gl = lane >> 4;
+    const bool sparse = a.topk > 0;
     f32x4 o[8][4];  // [output column tile of this wave][row tile]
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      asm volatile("" : "+a"(o[dt][0]), "+a"(o[dt][1]), "+a"(o[dt][2]), "+a"(o[dt][3]));
 
-    // ---- prologue: row entries of the first steps, then three bundles in flight --------------
-    const bool sparse = a.topk > 0;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // LDS rings free
+    // ---- prologue: row entries of the first steps, then bundles q0 and q0 + 1 ---------------
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // rings free
     if (sparse) {
 #pragma unroll
       for (int i = 0; i < 6; ++i) idx_fetch(q0 + i);
@@ -755,176 +887,66 @@ struct Col64 {
 #pragma unroll
     for (int i = 0; i < 3; ++i) page_fetch(q0 + i);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // bundle x: rows of step x (entries landed), block-table entries of x + 3, index entries of x + 6
-    auto bundle = [&](int x) -> uint32_t {
-      const int j = row_j(x);
-      const int page = ri_read(pg_slot(x));
-      bool v;
-      const uint64_t base = row_base(j, x < qend && row_ok(x, j), page, &v);
-      const uint32_t m = (uint32_t)__ballot(v);
-      issue(x & 3, base);
-      page_fetch(x + 3);
-      if (sparse) idx_fetch(x + 6);
-      return m;
-    };
-    uint32_t vm[3];  // row-valid masks of the steps in flight
-    vm[0] = bundle(q0);
-    vm[1] = bundle(q0 + 1);
-    vm[2] = bundle(q0 + 2);
-    const bool dense_mask = (a.topk == 0) && (a.causal || a.window > 0);
+    bundle(q0);
+    bundle(q0 + 1);
+    // bundle q0 landed, bundle q0 + 1 may be in flight
+    if (sparse) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaOps + 2) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaOps + 1) : "memory");
+    lds_barrier();
 
-    for (int q = q0; q < qend; ++q) {
-      const int sl = q & 3;
-      const uint32_t vmask = vm[0];
-      // bundle q landed, bundles q + 1 and q + 2 may still be in flight
-      if (sparse) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * (kDmaOps + 2)) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * (kDmaOps + 1)) : "memory");
-      lds_barrier();  // every wave's rows of step q landed; slot q - 1 is free for bundle q + 3
-      vm[0] = vm[1];
-      vm[1] = vm[2];
-      vm[2] = bundle(q + 3);
-      const uint32_t sa = sl * kSlot;
-      const uint32_t sb = sa + kSlotA;
-
-      // ---- S^T = K Q^T: 32 step rows x this wave's 16 rows ---------------------------------
-      uint32_t kaddr[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) kaddr[kt] = sa + (16 * kt + nl) * kRowStrideA + 16 * gl;
-      auto k_operand = [&](int kt, int ks) -> bf16x8 {
-        if (ks < 16) return lds_read_b128(sm, kaddr[kt] + 64 * ks);
-        const int row = 16 * kt + nl;
-        const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
-        return lds_read_b128(sm, sb + row * 128 + 16 * c);
-      };
-      constexpr int D = 4;  // operand steps in flight
-      bf16x8 ka[D][2];
-#pragma unroll
-      for (int i = 0; i < D - 1; ++i)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) ka[i][kt] = k_operand(kt, i);
-      f32x4 sacc[2];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + D - 1 < KS) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) ka[(ks + D - 1) % D][kt] = k_operand(kt, ks + D - 1);
-        }
-        if (ks == KS - 1) {
-          mfma_s_last2(sacc[0], sacc[1], ka[ks % D][0], ka[ks % D][1], qr[ks]);
-        } else {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            if (ks == 0) mfma_s0(sacc[kt], ka[0][kt], qr[0]);
-            else mfma_s(sacc[kt], ka[ks % D][kt], qr[ks]);
-          }
-        }
-      }
-
-      // ---- masks -----------------------------------------------------------------------------
-      const bool tail = 32 * (q + 1) > n;
-      bool need_mask = tail || dense_mask;
-      if (sparse) need_mask = (vmask != ~0u);
-      if (need_mask) {
-        const int causal_hi = a.causal ? 0 : (1 << 30);
-        const int win = a.window > 0 ? a.window : (1 << 30);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = 16 * kt + 4 * gl + e;
-            const int k = 32 * q + row;
-            const int j = j0 + k;
-            const bool ok = sparse ? (((vmask >> row) & 1u) != 0)
-                                   : (k < n && j <= qpos + causal_hi && j >= qpos - win + 1);
-            sacc[kt][e] = ok ? sacc[kt][e] : kNegInf;
-          }
-      }
-
-      // ---- softmax of this wave's rows (base 2, lazy reference maximum) ----------------------
-      float mx = kNegInf;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kt][e]);
-      mx = wave_max_groups(mx);
-      const float mnew = mx * a.scale_log2;  // -inf stays -inf (scale > 0)
-      const bool up = mnew > m_ref + kTau;
-      float alpha = 1.f;
-      if (up) {
-        alpha = __builtin_amdgcn_exp2f(m_ref - mnew);  // m_ref = -inf -> 0
-        m_ref = mnew;
-        l_acc *= alpha;
-      }
-      const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
-      bf16x8 pf;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], a.scale_log2, -mu));
-          lsum += pv;
-          pf[kt * 4 + e] = (__bf16)pv;
-        }
-      l_acc += lsum;
-      const bool wave_up = __any(up);
-      lds_barrier();  // PV of the previous step has read the P^T / factor buffers
-      *reinterpret_cast<LDS_AS bf16x8*>(sm + kPOff + (wave * 64 + lane) * 16) = pf;
-      if (gl == 0) *reinterpret_cast<LDS_AS float*>(sm + kAOff + 4 * (16 * wave + nl)) = alpha;
-      if (lane == 0) *reinterpret_cast<LDS_AS int*>(sm + kFOff + 4 * wave) = wave_up ? 1 : 0;
-      lds_barrier();
-
-      // ---- O^T[128 w .. 128 w + 127][64 rows] += V^T P^T -------------------------------------
-      {
-        const LDS_AS int* fl = reinterpret_cast<const LDS_AS int*>(sm + kFOff);
+    for (int t = q0; t <= qend; ++t) {
+      bundle(t + 2);  // into the slot of step t - 2, released at the last barrier
+      if (t > q0) {
+        const int u = t - 1;  // step accumulated now
+        const uint32_t pbo = (u & 1);
+        const LDS_AS int* fl = reinterpret_cast<const LDS_AS int*>(sm + kFOff + pbo * 16);
         if (fl[0] | fl[1] | fl[2] | fl[3]) {
           mfma_drain_acc(o);
 #pragma unroll
           for (int ht = 0; ht < 4; ++ht) {
-            const float al = *reinterpret_cast<const LDS_AS float*>(sm + kAOff + 4 * (16 * ht + nl));
+            const float al = *reinterpret_cast<const LDS_AS float*>(sm + kAOff + pbo * 256 + 4 * (16 * ht + nl));
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
               o[dt][ht] *= al;
+              asm volatile("" : "+a"(o[dt][ht]));  // back to its accumulation registers now
               __builtin_amdgcn_sched_barrier(0);
             }
           }
         }
+        bf16x8 pb[4];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+          pb[ht] = *reinterpret_cast<const LDS_AS bf16x8*>(sm + kPOff + pbo * 4096 + (ht * 64 + lane) * 16);
+        const uint32_t vbase = (u & 3) * kSlot + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (lane & 3) + 256 * vw;
+        auto v_operand = [&](int dt) -> bf16x8 {
+          const uint32_t ad = vbase + 32 * dt;
+          const bf16x4 v0 = lds_read_tr(sm, ad);
+          const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
+          return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 va[3];
+        va[0] = v_operand(0);
+        va[1] = v_operand(1);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          if (dt + 2 < 8) va[(dt + 2) % 3] = v_operand(dt + 2);
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) mfma_o(o[dt][ht], va[dt % 3], pb[ht]);
+        }
       }
-      bf16x8 pb[4];
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht)
-        pb[ht] = *reinterpret_cast<const LDS_AS bf16x8*>(sm + kPOff + (ht * 64 + lane) * 16);
-      const uint32_t vbase = sa + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (lane & 3) + 256 * wave;
-      auto v_operand = [&](int dt) -> bf16x8 {
-        const uint32_t ad = vbase + 32 * dt;
-        const bf16x4 v0 = lds_read_tr(sm, ad);
-        const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
-        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      bf16x8 va[3];
-      va[0] = v_operand(0);
-      va[1] = v_operand(1);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        if (dt + 2 < 8) va[(dt + 2) % 3] = v_operand(dt + 2);
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) mfma_o(o[dt][ht], va[dt % 3], pb[ht]);
-      }
+      // bundle t + 1 landed (K of the next step), bundle t + 2 may be in flight
+      if (sparse) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaOps + 2) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaOps + 1) : "memory");
+      lds_barrier();
     }
     // the last bundles (zero-row reads) must land before the slots are reused
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     mfma_drain_acc(o);
+    lds_barrier();  // score waves' statistics published
 
-    // ---- epilogue: row statistics to every wave, then each wave writes its columns ----------
-    {
-      const float lt = wave_sum_groups(l_acc);
-      if (gl == 0) {
-        *reinterpret_cast<LDS_AS float*>(sm + kLOff + 4 * (wave * 16 + nl)) = lt;
-        *reinterpret_cast<LDS_AS float*>(sm + kLOff + 256 + 4 * (wave * 16 + nl)) = m_ref;
-      }
-    }
-    __syncthreads();
+    // ---- epilogue: each value wave writes its 128 columns of all 64 rows ---------------------
     const bool final_out = (nsplit == 1);
+    const int tile0 = mt * 64;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
       const int hrow = ht * 16 + nl;
@@ -934,7 +956,7 @@ struct Col64 {
       if (r < a.R) {
         float lse_nat, scale;
         row_norm(r, m2, lt, final_out, &lse_nat, &scale);
-        const int col0 = 128 * wave + 4 * gl;
+        const int col0 = 128 * vw + 4 * gl;
         if (final_out) {
           uint16_t* dst = a.out + ((int64_t)g * a.R + r) * kDv + col0;
 #pragma unroll
@@ -946,7 +968,7 @@ struct Col64 {
             *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
             __builtin_amdgcn_sched_barrier(0);
           }
-          if (wave == 0 && gl == 0) a.lse[lse_index(r)] = lse_nat;
+          if (vw == 0 && gl == 0) a.lse[lse_index(r)] = lse_nat;
         } else {
           float* dst = a.part_o + ((int64_t)s * a.R + r) * kDv + col0;
 #pragma unroll
@@ -954,11 +976,11 @@ struct Col64 {
             *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt][ht] * scale;
             __builtin_amdgcn_sched_barrier(0);
           }
-          if (wave == 0 && gl == 0) a.part_lse[(int64_t)s * a.R + r] = lse_nat;
+          if (vw == 0 && gl == 0) a.part_lse[(int64_t)s * a.R + r] = lse_nat;
         }
       }
     }
-    __syncthreads();  // statistics buffer and slots reused by the next split
+    lds_barrier();  // statistics buffer and slots reused by the next split
   }
 
   // LSE (natural log) and output scale of a row; the sink is folded in for final outputs.
@@ -1006,17 +1028,27 @@ __device__ __forceinline__ void unit_tile(int bid, int m_tiles, int* unit, int* 
 }
 
 template <int DQK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_col64_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[Col64<DQK>::LDS];
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_spec64_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Spec64<DQK>::LDS];
   const lds_ptr base = (lds_ptr)lds;
   int unit, mt;
   unit_tile(blockIdx.x, a.m_tiles, &unit, &mt);
   if (unit >= a.U) return;
   const int s0 = a.plan[a.unit_ptr_off + unit];
   const int s1 = a.plan[a.unit_ptr_off + unit + 1];
-  Col64<DQK> d(a, base);
-  for (int s = s0; s < s1; ++s) d.run_split(s, mt);
+  Spec64<DQK> d(a, base);
+  if (d.wave < 4) {
+    for (int s = s0; s < s1; ++s) {
+      d.load_split(s);
+      d.score_split(mt);
+    }
+  } else {
+    for (int s = s0; s < s1; ++s) {
+      d.load_split(s);
+      d.value_split(s, mt);
+    }
+  }
 }
 
 template <class C>
@@ -1046,11 +1078,11 @@ hipError_t launch_cfg(DecodeArgs a, hipStream_t s) {
 }
 
 template <int DQK>
-hipError_t launch_col64(DecodeArgs a, hipStream_t s) {
+hipError_t launch_spec64(DecodeArgs a, hipStream_t s) {
   a.m_tiles = (a.R + 63) / 64;
   const int64_t grid = (int64_t)((a.U + 7) / 8) * 8 * a.m_tiles;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_col64_kernel<DQK>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(decode_spec64_kernel<DQK>, dim3((unsigned)grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1058,7 +1090,7 @@ template <int DQK>
 hipError_t launch_dqk(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
   if (sh.R <= 16) return launch_cfg<Cfg<16, 4, DQK>>(a, s);
   if (sh.R <= 32) return launch_cfg<Cfg<16, 2, DQK>>(a, s);
-  return launch_col64<DQK>(a, s);
+  return launch_spec64<DQK>(a, s);
 }
 
 }  // namespace
