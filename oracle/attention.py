@@ -60,10 +60,12 @@ def visible_sparse(L: int, idx_row: np.ndarray, n: Optional[int] = None) -> np.n
 
 
 def attend(q_rows: np.ndarray, K: np.ndarray, sm_scale: float, d_v: int,
-           sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+           sink: Optional[np.ndarray] = None, abs_mass: bool = False):
     """Softmax attention of query rows [M, d_qk] over rows K [n, d_qk]; V = K[:, :d_v].
 
-    sink: optional [M] logits added to each row's denominator. Returns (O [M, d_v], LSE [M]).
+    sink: optional [M] logits added to each row's denominator. Returns (O [M, d_v], LSE [M]);
+    with abs_mass also A [M, d_v] = sum_j P_j |V_j|, the weighted magnitude of the terms that
+    make up O (the scale of any error proportional to the probabilities, e.g. their rounding).
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -72,7 +74,7 @@ def attend(q_rows: np.ndarray, K: np.ndarray, sm_scale: float, d_v: int,
     if n == 0:
         O = np.zeros((M, d_v))
         lse = np.full(M, -np.inf) if sink is None else np.asarray(sink, dtype=np.float64).copy()
-        return O, lse
+        return (O, lse, np.zeros((M, d_v))) if abs_mass else (O, lse)
     S = sm_scale * (q_rows @ K.T)                      # [M, n]
     m = S.max(axis=1)
     if sink is not None:
@@ -84,13 +86,15 @@ def attend(q_rows: np.ndarray, K: np.ndarray, sm_scale: float, d_v: int,
     lse = m + np.log(denom)
     P = np.exp(S - lse[:, None])
     O = P @ K[:, :d_v]
+    if abs_mass:
+        return O, lse, P @ np.abs(K[:, :d_v])
     return O, lse
 
 
 def mla_decode(q: np.ndarray, rows_of: Callable[[int], np.ndarray], seqlens, sm_scale: float,
                d_v: int = 512, causal: bool = False, window: int = 0,
                indices: Optional[np.ndarray] = None, topk_lens: Optional[np.ndarray] = None,
-               sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+               sink: Optional[np.ndarray] = None, abs_mass: bool = False):
     """Reference decode over all requests.
 
     q        [B, Sq, H, d_qk] (any float dtype; widened to float64)
@@ -99,12 +103,14 @@ def mla_decode(q: np.ndarray, rows_of: Callable[[int], np.ndarray], seqlens, sm_
     indices  optional [B, Sq, topk] request-local positions (sparse mode)
     topk_lens optional [B * Sq] number of leading index entries used per token
     sink     optional [H] per-head sink logits
-    Returns O [B, Sq, H, d_v] and LSE [B, H, Sq], float64.
+    Returns O [B, Sq, H, d_v] and LSE [B, H, Sq], float64; with abs_mass also A [B, Sq, H, d_v]
+    (see attend).
     """
     q = np.asarray(q, dtype=np.float64)
     B, Sq, H, _ = q.shape
     O = np.zeros((B, Sq, H, d_v))
     LSE = np.zeros((B, H, Sq))
+    A = np.zeros((B, Sq, H, d_v)) if abs_mass else None
     sink_v = None if sink is None else np.asarray(sink, dtype=np.float64)
     for b in range(B):
         L = int(seqlens[b])
@@ -115,7 +121,9 @@ def mla_decode(q: np.ndarray, rows_of: Callable[[int], np.ndarray], seqlens, sm_
                 J = visible_sparse(L, np.asarray(indices)[b, t], n)
             else:
                 J = visible_dense(L, Sq, t, causal, window)
-            o, lse = attend(q[b, t], K[J], sm_scale, d_v, sink_v)
-            O[b, t] = o
-            LSE[b, :, t] = lse
-    return O, LSE
+            res = attend(q[b, t], K[J], sm_scale, d_v, sink_v, abs_mass)
+            O[b, t] = res[0]
+            LSE[b, :, t] = res[1]
+            if abs_mass:
+                A[b, t] = res[2]
+    return (O, LSE, A) if abs_mass else (O, LSE)

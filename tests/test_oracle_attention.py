@@ -251,15 +251,15 @@ def test_planted_mistakes_are_caught(monkeypatch):
     bo, bl = brute.decode_token(q[0, 0].tolist(), K.tolist(), [0, 1, 2, 3], 0.37, 4, sink.tolist())
     good = attention.attend
 
-    def no_scale(qr, KK, s, dv, sk=None):
+    def no_scale(qr, KK, s, dv, sk=None, am=False):
         return good(qr, KK, 1.0, dv, sk)
 
-    def sink_dropped_from_lse(qr, KK, s, dv, sk=None):
+    def sink_dropped_from_lse(qr, KK, s, dv, sk=None, am=False):
         O, _ = good(qr, KK, s, dv, sk)
         _, lse = good(qr, KK, s, dv, None)
         return O, lse
 
-    def v_from_tail(qr, KK, s, dv, sk=None):
+    def v_from_tail(qr, KK, s, dv, sk=None, am=False):
         O, lse = good(qr, KK, s, dv, sk)
         P = np.exp(s * (qr @ KK.T) - lse[:, None])
         return P @ KK[:, -dv:], lse
@@ -270,3 +270,17 @@ def test_planted_mistakes_are_caught(monkeypatch):
         caught = not (np.allclose(O[0, 0], bo, atol=1e-9) and np.allclose(lse[0, :, 0], bl, atol=1e-9))
         assert caught, bad.__name__
     monkeypatch.setattr(attention, "attend", good)
+
+
+def test_abs_mass_closed_forms():
+    """The weighted magnitude sum_j P_j |V_j|: equals |O| when every V entry of a column has one
+    sign, and equals the plain mean of |V| for uniform scores."""
+    rng = np.random.default_rng(41)
+    K = np.abs(rng.standard_normal((7, 8)))
+    q = rng.standard_normal((3, 8))
+    O, _, A = attention.attend(q, K, 0.3, 5, abs_mass=True)
+    np.testing.assert_allclose(A, np.abs(O), rtol=1e-12)
+    K2 = rng.standard_normal((7, 8))
+    O2, lse2, A2 = attention.attend(np.zeros((2, 8)), K2, 0.3, 5, abs_mass=True)
+    np.testing.assert_allclose(A2, np.broadcast_to(np.abs(K2[:, :5]).mean(axis=0), (2, 5)), rtol=1e-12)
+    np.testing.assert_allclose(lse2, np.log(7.0), rtol=1e-12)
