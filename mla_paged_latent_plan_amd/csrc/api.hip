@@ -146,7 +146,6 @@ int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void*
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return MLA_ERR_SHAPE;
   const size_t need = partial_size(sh);
   if (partials == nullptr || partial_bytes < need) return MLA_ERR_WORKSPACE;
-  if (sh.fmt != MLA_KV_BF16) return MLA_ERR_FORMAT;  // fp8 rows: not available yet
   const PlanLayout lay = PlanLayout::make(sh.G, sh.U);
   mla::DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -164,6 +163,7 @@ int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void*
   a.page_stride = sh.page_stride;
   a.num_pages = sh.num_pages;
   a.row_bytes = sh.row_bytes;
+  a.scale_off = (int64_t)sh.page_size * sh.row_bytes;
   a.grp_ptr_off = lay.grp_ptr;
   a.unit_ptr_off = lay.unit_ptr;
   a.grp_rows_off = lay.grp_rows;

@@ -33,6 +33,8 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
@@ -92,6 +94,54 @@ __device__ __forceinline__ float wave_sum_groups(float v) {
   v += __shfl_xor(v, 16, 64);
   v += __shfl_xor(v, 32, 64);
   return v;
+}
+
+// Same reductions across the four 16-lane rows with the VALU lane swaps (no LDS round trip).
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// ue8m0 scale byte -> 2^(s - 127) as a float (byte 0 is the subnormal 2^-127, byte 255 is NaN).
+__device__ __forceinline__ float ue8m0_f32(uint32_t s) {
+  const uint32_t bits = (s == 0u) ? 0x00400000u : ((s == 255u) ? 0x7FC00000u : (s << 23));
+  return __uint_as_float(bits);
+}
+// Eight e4m3 bytes (little-endian order in w) of one scale group -> bf16, times the group scale.
+// The product of an e4m3 value and a power of two is exact in bf16.
+__device__ __forceinline__ bf16x8 fp8x8_scaled(uint32_t w0, uint32_t w1, float sc) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+// Eight e4m3 bytes from eight different rows -> bf16, each times its own row's scale.
+__device__ __forceinline__ bf16x8 fp8x8_rowscaled(uint32_t w0, uint32_t w1, const float (&sc)[8]) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+  return bf16x8{(__bf16)(a[0] * sc[0]), (__bf16)(a[1] * sc[1]), (__bf16)(b[0] * sc[2]), (__bf16)(b[1] * sc[3]),
+                (__bf16)(c[0] * sc[4]), (__bf16)(c[1] * sc[5]), (__bf16)(d[0] * sc[6]), (__bf16)(d[1] * sc[7])};
+}
+// fp8 latent region: 512-byte rows, 16-byte chunk c of row r stored at chunk c ^ swz_n(r). Keeps
+// the K-operand reads (16 consecutive rows) and the transposed V reads (rows 4g..4g+3 and
+// 16+4g..16+4g+3) free of bank conflicts.
+__device__ __forceinline__ int swz_n(int row) { return (row & 15) ^ ((row >> 4) << 3); }
+
+__device__ __forceinline__ bf16x8 lds_read_tr8_nz(LDS_AS uint32_t* __restrict__ p) {
+  typedef __attribute__((ext_vector_type(2))) int i32x2;
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<LDS_AS i32x2*>(p));
+  return __builtin_bit_cast(bf16x8, u32x4{(uint32_t)v[0], (uint32_t)v[1], 0u, 0u});
 }
 
 __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
@@ -605,6 +655,49 @@ __device__ __forceinline__ void mfma_sq_last2(f32x4& c0, f32x4& c1, const bf16x8
       : "+v"(c0), "+v"(c1)
       : "v"(a0), "v"(a1), "a"(b));
 }
+// MFMAs whose operands were just written by VALU instructions (fp8 -> bf16 conversions): a VALU
+// write of a VGPR needs two wait states before an MFMA reads it, which the compiler does not insert
+// for inline assembly. Each statement waits three and takes every converted operand as an input.
+__device__ __forceinline__ void mfma_sq2_cvt0(f32x4& c0, f32x4& c1, const bf16x8& a0, const bf16x8& a1,
+                                              const bf16x8& b) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %4, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %4, 0"
+      : "=&v"(c0), "=&v"(c1)
+      : "v"(a0), "v"(a1), "a"(b));
+}
+__device__ __forceinline__ void mfma_sq2_cvt(f32x4& c0, f32x4& c1, const bf16x8& a0, const bf16x8& a1,
+                                             const bf16x8& b) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %4, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %4, %1"
+      : "+v"(c0), "+v"(c1)
+      : "v"(a0), "v"(a1), "a"(b));
+}
+__device__ __forceinline__ void mfma_sq2_cvt_last(f32x4& c0, f32x4& c1, const bf16x8& a0,
+                                                  const bf16x8& a1, const bf16x8& b) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %4, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %4, %1\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 2"
+      : "+v"(c0), "+v"(c1)
+      : "v"(a0), "v"(a1), "a"(b));
+}
+__device__ __forceinline__ void mfma_o4_cvt(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& c3, const bf16x8& a,
+                                            const bf16x8& b0, const bf16x8& b1, const bf16x8& b2,
+                                            const bf16x8& b3) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %5, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %6, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %4, %7, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %4, %8, %3"
+      : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
+      : "v"(a), "v"(b0), "v"(b1), "v"(b2), "v"(b3));
+}
 template <int N>
 __device__ __forceinline__ void mfma_drain_acc(f32x4 (&o)[N][4]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" ::: "memory");
@@ -630,13 +723,21 @@ __device__ __forceinline__ void mfma_drain_acc(f32x4 (&o)[N][4]) {
 // so no register waits on an in-flight load; their addresses are clamped and the values validated
 // when consumed. Every bundle holds the same number of memory operations, so "bundle x has landed"
 // is an exact vmcnt.
-template <int DQK>
+template <int DQK, bool FP8>
 struct Spec64 {
-  static constexpr bool HAS_B = DQK > 512;
-  static constexpr int KS = DQK / 32;
+  // bf16 rows: latent region = the first 512 values (1056-byte LDS rows), RoPE region = values
+  // 512..575 when present. fp8 rows: latent region = the kNope e4m3 bytes (512-byte LDS rows,
+  // swizzled), RoPE region = the 64 bf16 tail values, then the eight ue8m0 scale bytes per row.
+  static constexpr int kNope = DQK - 64;                   // fp8 values per row
+  static constexpr bool HAS_B = FP8 || DQK > 512;          // RoPE region present
+  static constexpr int KS = DQK / 32;                      // 32-wide k steps of QK^T
+  static constexpr int KSN = FP8 ? kNope / 32 : 16;        // k steps read from the latent region
+  static constexpr int kRopeSrc = FP8 ? kNope : 1024;      // byte offset of the RoPE tail in a row
   static constexpr int kRows = 32;                         // rows per slot / step
-  static constexpr int kSlotA = kRows * kRowStrideA;
-  static constexpr int kSlot = kSlotA + (HAS_B ? kRows * 128 : 0);
+  static constexpr int kRowA = FP8 ? 512 : kRowStrideA;
+  static constexpr int kSlotA = kRows * kRowA;
+  static constexpr int kScOff = kSlotA + kRows * 128;      // fp8: scale bytes [32][8]
+  static constexpr int kSlot = FP8 ? kScOff + kRows * 8 : kSlotA + (HAS_B ? kRows * 128 : 0);
   static constexpr uint32_t kPOff = 4 * kSlot;             // P^T fragments [2][4 row tiles][64]
   static constexpr uint32_t kAOff = kPOff + 2 * 4096;      // rescale factors [2][64]
   static constexpr uint32_t kFOff = kAOff + 2 * 256;       // rescale flags [2][4]
@@ -645,7 +746,7 @@ struct Spec64 {
   static constexpr uint32_t kRiOff = kLOff + 512;          // per value wave: block-table entries
   static constexpr int kRiWave = 4 * 32 + 8 * 32;          //   [4][8], index entries [8][8]
   static constexpr int LDS = kRiOff + 4 * kRiWave;
-  static constexpr int kDmaOps = 8 + (HAS_B ? 1 : 0);     // row LDS-DMA instructions per bundle
+  static constexpr int kDmaOps = FP8 ? 6 : 8 + (HAS_B ? 1 : 0);  // row LDS-DMA instructions per bundle
 
   const DecodeArgs& a;
   lds_ptr sm;
@@ -685,7 +786,8 @@ struct Spec64 {
     const int pi = min(max(j >> a.ps_log2, 0), a.max_pages - 1);
     dma_dword(a.block_table + (int64_t)b * a.max_pages + pi, pg_slot(x));
   }
-  __device__ __forceinline__ uint64_t row_base(int x, bool* valid) const {
+  // Global address of the row (and, for fp8 rows, of its scale slot); invalid rows read the zero row.
+  __device__ __forceinline__ uint64_t row_base(int x, bool* valid, uint64_t* scale_base) const {
     const int j = row_j(x);
     const int page = ri_read(pg_slot(x));
     const int k = 32 * x + vrow();
@@ -693,23 +795,41 @@ struct Spec64 {
     if (a.topk > 0) ok = ok && j >= 0 && j < L;
     ok = ok && page >= 0 && (int64_t)page < a.num_pages;
     *valid = ok;
-    if (!ok) return (uint64_t)(uintptr_t)a.zero_row;
+    if (!ok) {
+      *scale_base = (uint64_t)(uintptr_t)a.zero_row;
+      return (uint64_t)(uintptr_t)a.zero_row;
+    }
     const int slot = j & ((1 << a.ps_log2) - 1);
-    return (uint64_t)(uintptr_t)(a.cache + (int64_t)page * a.page_stride + (int64_t)slot * a.row_bytes);
+    const uint8_t* pg = a.cache + (int64_t)page * a.page_stride;
+    *scale_base = (uint64_t)(uintptr_t)(pg + a.scale_off + 8 * slot);
+    return (uint64_t)(uintptr_t)(pg + (int64_t)slot * a.row_bytes);
   }
   __device__ __forceinline__ void bundle(int x) const {
     bool v;
-    const uint64_t base = row_base(x, &v);
+    uint64_t sbase;
+    const uint64_t base = row_base(x, &v, &sbase);
     const uint32_t m = (uint32_t)__ballot(v) & 0xFFu;
     if (lane == 0) *reinterpret_cast<LDS_AS uint8_t*>(sm + kMOff + 4 * (x & 3) + (wave - 4)) = (uint8_t)m;
     const uint32_t sa = (x & 3) * kSlot;
     const int r0 = 8 * (wave - 4);
+    if constexpr (FP8) {
+      // latent bytes: two 512-byte rows per instruction, chunks swizzled by row
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint64_t rb = readlane64(base, i);
-      const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 16 * lane;
-      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + (r0 + i) * kRowStrideA),
-                                       16, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t b0 = readlane64(base, 2 * i), b1 = readlane64(base, 2 * i + 1);
+        const uint64_t rb = (lane < 32) ? b0 : b1;
+        const int row = r0 + 2 * i + (lane >> 5);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 16 * ((lane & 31) ^ swz_n(row));
+        __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + (r0 + 2 * i) * 512), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint64_t rb = readlane64(base, i);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 16 * lane;
+        __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + (r0 + i) * kRowStrideA),
+                                         16, 0, 0);
+      }
     }
     if constexpr (HAS_B) {
       const int r = r0 + (lane >> 3);
@@ -717,9 +837,18 @@ struct Spec64 {
       const uint32_t lo = __shfl((uint32_t)base, lane >> 3, 64);
       const uint32_t hi = __shfl((uint32_t)(base >> 32), lane >> 3, 64);
       const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo)) +
-                           1024 + 16 * c;
+                           kRopeSrc + 16 * c;
       __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + kSlotA + (wave - 4) * 1024),
                                        16, 0, 0);
+    }
+    if constexpr (FP8) {
+      // scale slots: 8 rows x 8 bytes, one dword per lane
+      const int sl = (lane >> 1) & 7;
+      const uint32_t lo = __shfl((uint32_t)sbase, sl, 64);
+      const uint32_t hi = __shfl((uint32_t)(sbase >> 32), sl, 64);
+      const int32_t* src = reinterpret_cast<const int32_t*>((uintptr_t)(((uint64_t)hi << 32) | lo) + 4 * (lane & 1));
+      if (lane < 16)
+        __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + kScOff + r0 * 8), 4, 0, 0);
     }
     page_fetch(x + 3);
     if (a.topk > 0) idx_fetch(x + 6);
@@ -768,33 +897,66 @@ struct Spec64 {
         uint32_t kaddr[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) kaddr[kt] = sa + (16 * kt + nl) * kRowStrideA + 16 * gl;
-        auto k_operand = [&](int kt, int ks) -> bf16x8 {
-          if (ks < 16) return lds_read_b128(sm, kaddr[kt] + 64 * ks);
+        // raw operand of k step ks: bf16 values, or (fp8 latent steps) eight e4m3 bytes
+        auto k_raw = [&](int kt, int ks) -> bf16x8 {
           const int row = 16 * kt + nl;
-          const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
+          if (ks < KSN) {
+            if constexpr (FP8) {
+              const uint32_t ad = sa + row * 512 + 16 * ((2 * ks + (gl >> 1)) ^ swz_n(row)) + 8 * (gl & 1);
+              const u32x2 w = *reinterpret_cast<const LDS_AS u32x2*>(sm + ad);
+              return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], 0u, 0u});
+            } else {
+              return lds_read_b128(sm, kaddr[kt] + 64 * ks);
+            }
+          }
+          const int c = (4 * (ks - KSN) + gl) ^ swz_b(row);
           return lds_read_b128(sm, sb + row * 128 + 16 * c);
+        };
+        // fp8 rows: the scale bytes of the lane's two K rows
+        u32x2 ksc[2] = {u32x2{0u, 0u}, u32x2{0u, 0u}};
+        if constexpr (FP8) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            ksc[kt] = *reinterpret_cast<const LDS_AS u32x2*>(sm + sa + kScOff + 8 * (16 * kt + nl));
+        }
+        auto k_operand = [&](const bf16x8& raw, int kt, int ks) -> bf16x8 {
+          if constexpr (FP8) {
+            if (ks < KSN) {
+              const u32x4 w = __builtin_bit_cast(u32x4, raw);
+              const int gi = ks >> 1;  // 64-value scale group
+              const uint32_t sw = (gi < 4) ? ksc[kt][0] : ksc[kt][1];
+              return fp8x8_scaled(w[0], w[1], ue8m0_f32((sw >> (8 * (gi & 3))) & 0xFFu));
+            }
+          }
+          return raw;
         };
         constexpr int D = 4;  // operand steps in flight
         bf16x8 ka[D][2];
 #pragma unroll
         for (int i = 0; i < D - 1; ++i)
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) ka[i][kt] = k_operand(kt, i);
+          for (int kt = 0; kt < 2; ++kt) ka[i][kt] = k_raw(kt, i);
         f32x4 sacc[2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           if (ks + D - 1 < KS) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) ka[(ks + D - 1) % D][kt] = k_operand(kt, ks + D - 1);
+            for (int kt = 0; kt < 2; ++kt) ka[(ks + D - 1) % D][kt] = k_raw(kt, ks + D - 1);
           }
-          if (ks == KS - 1) {
-            mfma_sq_last2(sacc[0], sacc[1], ka[ks % D][0], ka[ks % D][1], qr[ks]);
+          const bf16x8 k0 = k_operand(ka[ks % D][0], 0, ks);
+          const bf16x8 k1 = k_operand(ka[ks % D][1], 1, ks);
+          if constexpr (FP8) {
+            if (ks == KS - 1) mfma_sq2_cvt_last(sacc[0], sacc[1], k0, k1, qr[ks]);
+            else if (ks == 0) mfma_sq2_cvt0(sacc[0], sacc[1], k0, k1, qr[0]);
+            else mfma_sq2_cvt(sacc[0], sacc[1], k0, k1, qr[ks]);
+          } else if (ks == KS - 1) {
+            mfma_sq_last2(sacc[0], sacc[1], k0, k1, qr[ks]);
+          } else if (ks == 0) {
+            mfma_sq0(sacc[0], k0, qr[0]);
+            mfma_sq0(sacc[1], k1, qr[0]);
           } else {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-              if (ks == 0) mfma_sq0(sacc[kt], ka[0][kt], qr[0]);
-              else mfma_sq(sacc[kt], ka[ks % D][kt], qr[ks]);
-            }
+            mfma_sq(sacc[0], k0, qr[ks]);
+            mfma_sq(sacc[1], k1, qr[ks]);
           }
         }
 
@@ -824,7 +986,7 @@ struct Spec64 {
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kt][e]);
-        mx = wave_max_groups(mx);
+        mx = rows_max(mx);
         const float mnew = mx * a.scale_log2;  // -inf stays -inf (scale > 0)
         const bool up = mnew > m_ref + kTau;
         float alpha = 1.f;
@@ -854,7 +1016,7 @@ struct Spec64 {
       lds_barrier();  // P^T of step t published; K slot of step t released
     }
     // ---- row statistics for the value waves --------------------------------------------------
-    const float lt = wave_sum_groups(l_acc);
+    const float lt = rows_sum(l_acc);
     if (gl == 0) {
       *reinterpret_cast<LDS_AS float*>(sm + kLOff + 4 * (wave * 16 + nl)) = lt;
       *reinterpret_cast<LDS_AS float*>(sm + kLOff + 256 + 4 * (wave * 16 + nl)) = m_ref;
@@ -917,21 +1079,65 @@ struct Spec64 {
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht)
           pb[ht] = *reinterpret_cast<const LDS_AS bf16x8*>(sm + kPOff + pbo * 4096 + (ht * 64 + lane) * 16);
-        const uint32_t vbase = (u & 3) * kSlot + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (lane & 3) + 256 * vw;
-        auto v_operand = [&](int dt) -> bf16x8 {
-          const uint32_t ad = vbase + 32 * dt;
-          const bf16x4 v0 = lds_read_tr(sm, ad);
-          const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
-          return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const uint32_t su = (u & 3) * kSlot;
+        // V^T operand rows: k slot 8 gl + e holds KV row 4 gl + e (e < 4) or 12 + 4 gl + e, the
+        // order of the P^T fragments
+        float vsc[2][8];  // fp8 rows: scale of each of the lane's eight KV rows, two column groups
+        if constexpr (FP8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int row = (e < 4) ? 4 * gl + e : 12 + 4 * gl + e;
+            const uint32_t sv = *reinterpret_cast<const LDS_AS uint16_t*>(sm + su + kScOff + 8 * row + 2 * vw);
+            vsc[0][e] = ue8m0_f32(sv & 0xFFu);
+            vsc[1][e] = ue8m0_f32(sv >> 8);
+          }
+        }
+        auto v_raw = [&](int dt) -> bf16x8 {
+          const int col0 = 128 * vw + 16 * dt;  // first output column of the tile
+          if constexpr (FP8) {
+            if (col0 < kNope) {
+              const int e = nl >> 1;
+              const int row = (e < 4) ? 4 * gl + e : 12 + 4 * gl + e;
+              const uint32_t ad = su + row * 512 + 16 * ((col0 >> 4) ^ swz_n(row)) + 8 * (nl & 1);
+              return lds_read_tr8_nz(reinterpret_cast<LDS_AS uint32_t*>(sm + ad));
+            }
+            // DSV4 rows: columns past the fp8 values are the RoPE tail (bf16)
+            const int row = 4 * gl + (nl >> 2);
+            const int c = 2 * ((col0 - kNope) >> 4) + ((nl & 3) >> 1);
+            const uint32_t ad = su + kSlotA + 16 * (c ^ swz_b(row)) + 8 * (nl & 1);
+            const int c2 = c ^ swz_b(row + 16);
+            const bf16x4 v0 = lds_read_tr(sm, ad + row * 128);
+            const bf16x4 v1 = lds_read_tr(sm, su + kSlotA + (row + 16) * 128 + 16 * c2 + 8 * (nl & 1));
+            return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          } else {
+            const uint32_t ad = su + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (lane & 3) + 2 * col0;
+            const bf16x4 v0 = lds_read_tr(sm, ad);
+            const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
+            return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        };
+        auto v_operand = [&](const bf16x8& raw, int dt) -> bf16x8 {
+          if constexpr (FP8) {
+            if (128 * vw + 16 * dt < kNope) {
+              const u32x4 w = __builtin_bit_cast(u32x4, raw);
+              return fp8x8_rowscaled(w[0], w[1], vsc[dt >> 2]);
+            }
+          }
+          return raw;
         };
         bf16x8 va[3];
-        va[0] = v_operand(0);
-        va[1] = v_operand(1);
+        va[0] = v_raw(0);
+        va[1] = v_raw(1);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          if (dt + 2 < 8) va[(dt + 2) % 3] = v_operand(dt + 2);
+          if (dt + 2 < 8) va[(dt + 2) % 3] = v_raw(dt + 2);
+          const bf16x8 vop = v_operand(va[dt % 3], dt);
+          if constexpr (FP8) {
+            mfma_o4_cvt(o[dt][0], o[dt][1], o[dt][2], o[dt][3], vop, pb[0], pb[1], pb[2], pb[3]);
+          } else {
 #pragma unroll
-          for (int ht = 0; ht < 4; ++ht) mfma_o(o[dt][ht], va[dt % 3], pb[ht]);
+            for (int ht = 0; ht < 4; ++ht) mfma_o(o[dt][ht], vop, pb[ht]);
+          }
         }
       }
       // bundle t + 1 landed (K of the next step), bundle t + 2 may be in flight
@@ -1027,17 +1233,17 @@ __device__ __forceinline__ void unit_tile(int bid, int m_tiles, int* unit, int* 
   *unit = (q / m_tiles) * 8 + x;
 }
 
-template <int DQK>
+template <int DQK, bool FP8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_spec64_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[Spec64<DQK>::LDS];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Spec64<DQK, FP8>::LDS];
   const lds_ptr base = (lds_ptr)lds;
   int unit, mt;
   unit_tile(blockIdx.x, a.m_tiles, &unit, &mt);
   if (unit >= a.U) return;
   const int s0 = a.plan[a.unit_ptr_off + unit];
   const int s1 = a.plan[a.unit_ptr_off + unit + 1];
-  Spec64<DQK> d(a, base);
+  Spec64<DQK, FP8> d(a, base);
   if (d.wave < 4) {
     for (int s = s0; s < s1; ++s) {
       d.load_split(s);
@@ -1077,26 +1283,26 @@ hipError_t launch_cfg(DecodeArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DQK>
+template <int DQK, bool FP8>
 hipError_t launch_spec64(DecodeArgs a, hipStream_t s) {
   a.m_tiles = (a.R + 63) / 64;
   const int64_t grid = (int64_t)((a.U + 7) / 8) * 8 * a.m_tiles;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_spec64_kernel<DQK>, dim3((unsigned)grid), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((decode_spec64_kernel<DQK, FP8>), dim3((unsigned)grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 template <int DQK>
 hipError_t launch_dqk(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
+  if (sh.fmt != 0) return launch_spec64<DQK, true>(a, s);  // fp8 rows: 64-row tiles for any R
   if (sh.R <= 16) return launch_cfg<Cfg<16, 4, DQK>>(a, s);
   if (sh.R <= 32) return launch_cfg<Cfg<16, 2, DQK>>(a, s);
-  return launch_spec64<DQK>(a, s);
+  return launch_spec64<DQK, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
-  if (sh.fmt != 0) return hipErrorNotSupported;
   return sh.d_qk == 576 ? launch_dqk<576>(a, sh, s) : launch_dqk<512>(a, sh, s);
 }
 

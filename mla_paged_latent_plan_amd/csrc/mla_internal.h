@@ -74,6 +74,7 @@ struct DecodeArgs {
   uint16_t* out;
   float* lse;
   int64_t page_stride, num_pages, row_bytes;
+  int64_t scale_off;  // fp8 rows: byte offset of a page's scale slots (page_size * row_bytes)
   int64_t grp_ptr_off, unit_ptr_off, grp_rows_off, splits_off;
   int B, Sq, H, R, G, U, m_tiles, ps_log2, max_pages, topk, causal, window;
   float scale_log2;  // sm_scale * log2(e)

@@ -38,6 +38,23 @@ CASES = {
     "sparse_h16_lens": (Spec("sparse_h16_lens", batch=2, q_len=2, num_heads=16, page_size=16,
                              seqlens=(400, 90), topk=128, sm_scale=S, seed=17),
                         np.array([100, 0, 128, 64])),
+    # fp8 rows (e4m3 values, one ue8m0 scale per 64, bf16 RoPE tail)
+    "fp8_h128_edges": (Spec("fp8_h128_edges", batch=6, q_len=1, num_heads=128, page_size=64,
+                            kv_format="fp8", seqlens=(1, 63, 64, 65, 700, 2001), sm_scale=S,
+                            seed=31), None),
+    "fp8_h16_page16": (Spec("fp8_h16_page16", batch=7, q_len=1, num_heads=16, page_size=16,
+                            kv_format="fp8", seqlens=(0, 1, 15, 130, 511, 1000, 64), sm_scale=S,
+                            scale_exp_range=(-6, 6), seed=32), None),
+    "fp8_d512_verify": (Spec("fp8_d512_verify", batch=4, q_len=4, num_heads=16, d_qk=512,
+                             kv_format="fp8", page_size=64, seqlens=(3, 131, 1000, 4),
+                             causal=True, window=128, sink=True, sm_scale=1 / math.sqrt(512),
+                             seed=33), None),
+    "fp8_d512_h64": (Spec("fp8_d512_h64", batch=3, q_len=2, num_heads=64, d_qk=512,
+                          kv_format="fp8", page_size=64, seqlens=(77, 700, 129), causal=True,
+                          sm_scale=1 / math.sqrt(512), seed=34), None),
+    "fp8_sparse_h128": (Spec("fp8_sparse_h128", batch=2, q_len=1, num_heads=128, page_size=64,
+                             kv_format="fp8", seqlens=(5000, 3), topk=300, sm_scale=S, seed=35),
+                        None),
 }
 
 
@@ -60,8 +77,8 @@ def test_parity(name, cus):
     num_cus = {"device": None, "one": 1, "many": 1024}[cus]
     print(f"[gpu] parity {name} cus={cus}", flush=True)
     out, lse, plan, used = H.run_gpu(wl, num_cus)
-    O, L = H.oracle_of(wl)
-    m = H.metrics(out, lse, O, L)
+    O, L, A = H.oracle_of(wl, abs_mass=True)
+    m = H.metrics(out, lse, O, L, A)
     print(f"[gpu]   {m}", flush=True)
     H.assert_parity(m, ctx=f"{name}/{cus}")
     want = H.plan_words(wl, used)
@@ -104,6 +121,23 @@ def test_uniform_scores_exact_mean():
         np.testing.assert_allclose(lse[b, :, 0].numpy(), math.log(L), atol=1e-4)
 
 
+def test_fp8_extreme_scales_uniform_scores():
+    """q = 0 over fp8 rows whose scale exponents span [-100, 100]: O is the mean of the dequantised
+    V rows (every exponent decoded exactly) and LSE = ln(count)."""
+    spec = Spec("fp8_wide_scales", batch=2, q_len=1, num_heads=16, page_size=64, kv_format="fp8",
+                seqlens=(70, 300), scale_exp_range=(-100, 100), sm_scale=S, seed=23)
+    wl = make(spec)
+    wl.q = torch.zeros_like(wl.q)
+    print("[gpu] fp8 extreme scales", flush=True)
+    out, lse, _, _ = H.run_gpu(wl)
+    O, L, A = H.oracle_of(wl, abs_mass=True)
+    m = H.metrics(out, lse, O, L, A)
+    print(f"[gpu]   {m}", flush=True)
+    H.assert_parity(m, ctx="fp8 extreme scales")
+    for b in range(2):
+        np.testing.assert_allclose(lse[b, :, 0].numpy(), math.log(int(wl.seqlens[b])), atol=1e-4)
+
+
 def test_sparse_arange_equals_dense():
     spec = Spec("sp_eq", batch=2, q_len=1, num_heads=128, page_size=64, seqlens=(300, 64),
                 sm_scale=S, seed=22)
@@ -119,14 +153,14 @@ def test_sparse_arange_equals_dense():
     assert m["max_abs"] <= 1e-2 and m["lse_max_abs"] <= 1e-4, m
 
 
-@pytest.mark.parametrize("cfg", [2, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_full_size_configs(cfg):
     """The benchmark workloads at their full sizes, in the launch configuration the bench uses."""
     wl = make(CONFIGS[cfg])
     print(f"[gpu] full-size config {cfg}", flush=True)
     out, lse, plan, used = H.run_gpu(wl)
-    O, L = H.oracle_of(wl)
-    m = H.metrics(out, lse, O, L)
+    O, L, A = H.oracle_of(wl, abs_mass=True)
+    m = H.metrics(out, lse, O, L, A)
     print(f"[gpu]   {m}", flush=True)
     H.assert_parity(m, ctx=f"config {cfg}")
     want = H.plan_words(wl, used)
