@@ -14,6 +14,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -107,15 +108,20 @@ def source_hash():
 
 
 def measured_traffic(workload_name):
-    """HBM bytes per decode launch from committed counter runs, if the kernels are unchanged."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    """HBM bytes per decode launch from the committed counter summary (FETCH_SIZE and WRITE_SIZE
+    runs, scaled by a plain copy's readings), if the kernel sources are unchanged since."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload_name}_hbm_counters.md")
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as f:
-        t = json.load(f)
-    if t.get("source_hash") != source_hash():
+        for line in f:
+            m = re.match(r"- (source_hash|hbm_bytes_per_launch): (\S+)", line.strip())
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("source_hash") != source_hash() or "hbm_bytes_per_launch" not in fields:
         return None
-    return int(t["hbm_bytes_per_launch"])
+    return int(fields["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(wl, target_s):
