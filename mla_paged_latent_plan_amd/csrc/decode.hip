@@ -24,6 +24,8 @@
 //   the common case. Row statistics are per lane (the head index runs along lanes).
 // - Masked rows (past the group's rows, invalid indices, pages outside the cache) are gathered
 //   from the plan's zero row, so no NaN from unused cache bytes can reach the accumulators.
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -738,6 +740,7 @@ struct Spec64 {
   static constexpr int kSlotA = kRows * kRowA;
   static constexpr int kScOff = kSlotA + kRows * 128;      // fp8: scale bytes [32][8]
   static constexpr int kSlot = FP8 ? kScOff + kRows * 8 : kSlotA + (HAS_B ? kRows * 128 : 0);
+  static_assert(kSlot % 256 == 0, "slot bases keep the low byte of in-slot offsets");
   static constexpr uint32_t kPOff = 4 * kSlot;             // P^T fragments [2][4 row tiles][64]
   static constexpr uint32_t kAOff = kPOff + 2 * 4096;      // rescale factors [2][64]
   static constexpr uint32_t kFOff = kAOff + 2 * 256;       // rescale flags [2][4]
@@ -846,7 +849,8 @@ struct Spec64 {
       const int sl = (lane >> 1) & 7;
       const uint32_t lo = __shfl((uint32_t)sbase, sl, 64);
       const uint32_t hi = __shfl((uint32_t)(sbase >> 32), sl, 64);
-      const int32_t* src = reinterpret_cast<const int32_t*>((uintptr_t)(((uint64_t)hi << 32) | lo) + 4 * (lane & 1));
+      // scale slots are 8-byte aligned: the dword offset is an OR into the low word
+      const int32_t* src = reinterpret_cast<const int32_t*>((uintptr_t)(((uint64_t)hi << 32) | (lo | (4u * (lane & 1)))));
       if (lane < 16)
         __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + kScOff + r0 * 8), 4, 0, 0);
     }
@@ -857,13 +861,14 @@ struct Spec64 {
   __device__ __forceinline__ void load_split(int s) {
     const int32_t* plan = a.plan;
     const int32_t* rec = plan + a.splits_off + 4 * (int64_t)s;
-    g = rec[0];
-    const int kb = rec[1], ke = rec[2];
-    j0 = plan[a.grp_rows_off + 2 * g];
-    n = plan[a.grp_rows_off + 2 * g + 1];
-    nsplit = plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g];
+    // split-wide values, kept in scalar registers (uniform across the workgroup)
+    g = __builtin_amdgcn_readfirstlane(rec[0]);
+    const int kb = __builtin_amdgcn_readfirstlane(rec[1]), ke = __builtin_amdgcn_readfirstlane(rec[2]);
+    j0 = __builtin_amdgcn_readfirstlane(plan[a.grp_rows_off + 2 * g]);
+    n = __builtin_amdgcn_readfirstlane(plan[a.grp_rows_off + 2 * g + 1]);
+    nsplit = __builtin_amdgcn_readfirstlane(plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g]);
     b = (a.topk > 0) ? g / a.Sq : g;
-    L = a.seqlens[b];
+    L = __builtin_amdgcn_readfirstlane(a.seqlens[b]);
     q0 = 2 * kb;
     qend = min(2 * ke, (n + kRows - 1) / kRows);  // steps holding at least one row
   }
@@ -1057,7 +1062,10 @@ struct Spec64 {
     lds_barrier();
 
     for (int t = q0; t <= qend; ++t) {
-      bundle(t + 2);  // into the slot of step t - 2, released at the last barrier
+      // bundle t + 2 goes into the slot of step t - 2, released at the last barrier. bf16 rows issue
+      // it first, so its issue overlaps the score waves' QK^T; fp8 rows issue it after PV, so that
+      // no wait in the PV section (register reloads of the converting code) waits on it.
+      if constexpr (!FP8) bundle(t + 2);
       if (t > q0) {
         const int u = t - 1;  // step accumulated now
         const uint32_t pbo = (u & 1);
@@ -1082,24 +1090,40 @@ struct Spec64 {
         const uint32_t su = (u & 3) * kSlot;
         // V^T operand rows: k slot 8 gl + e holds KV row 4 gl + e (e < 4) or 12 + 4 gl + e, the
         // order of the P^T fragments
-        float vsc[2][8];  // fp8 rows: scale of each of the lane's eight KV rows, two column groups
-        if constexpr (FP8) {
+        __builtin_assume(vw >= 0 && vw < 4);
+        // fp8 rows: scale bytes of the lane's eight KV rows, for the wave's two column groups
+        // (group 2 vw for tiles 0..3, 2 vw + 1 for tiles 4..7), read as needed
+        uint32_t vsb[8];
+        float vsc[8];
+        auto v_scale_bytes = [&](int grp) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int row = (e < 4) ? 4 * gl + e : 12 + 4 * gl + e;
-            const uint32_t sv = *reinterpret_cast<const LDS_AS uint16_t*>(sm + su + kScOff + 8 * row + 2 * vw);
-            vsc[0][e] = ue8m0_f32(sv & 0xFFu);
-            vsc[1][e] = ue8m0_f32(sv >> 8);
+            vsb[e] = *reinterpret_cast<const LDS_AS uint8_t*>(sm + su + kScOff + 8 * row + 2 * vw + grp);
           }
+        };
+        if constexpr (FP8) v_scale_bytes(0);
+        // fp8 latent tile dt of this wave: chunk 8 vw + dt of eight rows; with the row swizzle
+        // (8 vw + dt) ^ f = 8 (vw ^ (f >> 3)) + (dt ^ (f & 7)), so the lane's address is one base
+        // XOR 16 dt
+        uint32_t vb8 = 0;
+        if constexpr (FP8) {
+          const int e = nl >> 1;
+          const int row = (e < 4) ? 4 * gl + e : 12 + 4 * gl + e;
+          const int f = swz_n(row);
+          vb8 = (uint32_t)(row * 512 + 128 * (vw ^ (f >> 3)) + 8 * (nl & 1)) | (uint32_t)(16 * (f & 7));
+          vb8 += su;  // the slot base has no bits below 256, so the XOR below stays within the row
         }
-        auto v_raw = [&](int dt) -> bf16x8 {
+        // raw V operand: eight fp8 bytes (DSV3 rows), or room for a bf16 RoPE tile (DSV4 rows)
+        using VRaw = typename std::conditional<FP8, typename std::conditional<(kNope >= 512), u32x2, u32x4>::type,
+                                               bf16x8>::type;
+        auto v_raw = [&](int dt) -> VRaw {
           const int col0 = 128 * vw + 16 * dt;  // first output column of the tile
           if constexpr (FP8) {
             if (col0 < kNope) {
-              const int e = nl >> 1;
-              const int row = (e < 4) ? 4 * gl + e : 12 + 4 * gl + e;
-              const uint32_t ad = su + row * 512 + 16 * ((col0 >> 4) ^ swz_n(row)) + 8 * (nl & 1);
-              return lds_read_tr8_nz(reinterpret_cast<LDS_AS uint32_t*>(sm + ad));
+              const u32x4 w = __builtin_bit_cast(u32x4, lds_read_tr8_nz(reinterpret_cast<LDS_AS uint32_t*>(sm + (vb8 ^ (16u * dt)))));
+              if constexpr (kNope >= 512) return u32x2{w[0], w[1]};
+              else return w;
             }
             // DSV4 rows: columns past the fp8 values are the RoPE tail (bf16)
             const int row = 4 * gl + (nl >> 2);
@@ -1108,7 +1132,8 @@ struct Spec64 {
             const int c2 = c ^ swz_b(row + 16);
             const bf16x4 v0 = lds_read_tr(sm, ad + row * 128);
             const bf16x4 v1 = lds_read_tr(sm, su + kSlotA + (row + 16) * 128 + 16 * c2 + 8 * (nl & 1));
-            return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (kNope >= 512) return VRaw{0u, 0u};  // not reached: every column is fp8
+            else return __builtin_bit_cast(u32x4, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
           } else {
             const uint32_t ad = su + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (lane & 3) + 2 * col0;
             const bf16x4 v0 = lds_read_tr(sm, ad);
@@ -1116,22 +1141,32 @@ struct Spec64 {
             return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
           }
         };
-        auto v_operand = [&](const bf16x8& raw, int dt) -> bf16x8 {
+        auto v_operand = [&](const VRaw& raw, int dt) -> bf16x8 {
           if constexpr (FP8) {
-            if (128 * vw + 16 * dt < kNope) {
-              const u32x4 w = __builtin_bit_cast(u32x4, raw);
-              return fp8x8_rowscaled(w[0], w[1], vsc[dt >> 2]);
-            }
+            if (128 * vw + 16 * dt < kNope) return fp8x8_rowscaled(raw[0], raw[1], vsc);
+            if constexpr (kNope >= 512) return bf16x8{};  // not reached
+            else return __builtin_bit_cast(bf16x8, raw);
+          } else {
+            return raw;
           }
-          return raw;
         };
-        bf16x8 va[3];
-        va[0] = v_raw(0);
-        va[1] = v_raw(1);
+        // V operand tiles in flight: three for bf16 rows, two for fp8 rows (whose conversion
+        // already covers part of the read latency)
+        constexpr int VD = FP8 ? 2 : 3;
+        VRaw va[VD];
+#pragma unroll
+        for (int i = 0; i < VD - 1; ++i) va[i] = v_raw(i);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          if (dt + 2 < 8) va[(dt + 2) % 3] = v_raw(dt + 2);
-          const bf16x8 vop = v_operand(va[dt % 3], dt);
+          if (dt + VD - 1 < 8) va[(dt + VD - 1) % VD] = v_raw(dt + VD - 1);
+          if constexpr (FP8) {
+            if (dt == 0 || dt == 4) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) vsc[e] = ue8m0_f32(vsb[e]);
+            }
+            if (dt == 1) v_scale_bytes(1);
+          }
+          const bf16x8 vop = v_operand(va[dt % VD], dt);
           if constexpr (FP8) {
             mfma_o4_cvt(o[dt][0], o[dt][1], o[dt][2], o[dt][3], vop, pb[0], pb[1], pb[2], pb[3]);
           } else {
@@ -1140,6 +1175,7 @@ struct Spec64 {
           }
         }
       }
+      if constexpr (FP8) bundle(t + 2);
       // bundle t + 1 landed (K of the next step), bundle t + 2 may be in flight
       if (sparse) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaOps + 2) : "memory");
       else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaOps + 1) : "memory");
