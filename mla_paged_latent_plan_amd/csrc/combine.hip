@@ -9,7 +9,9 @@
 // mla_decode and are skipped.
 //
 // Launch: one workgroup of 256 threads per (group, 4 query rows); 64 threads per row, each
-// owning 8 consecutive columns, so partial rows are read as contiguous 2 KB lines.
+// owning 8 consecutive columns, so partial rows are read as contiguous 2 KB lines. Lane i reads
+// the LSE of split i (per chunk of 64 splits); four splits' rows are loaded before they are
+// accumulated.
 #include "mla_internal.h"
 
 namespace mla {
@@ -24,15 +26,27 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int g = blockIdx.y;
-  const int s0 = a.plan[a.grp_ptr_off + g];
-  const int s1 = a.plan[a.grp_ptr_off + g + 1];
+  const int s0 = __builtin_amdgcn_readfirstlane(a.plan[a.grp_ptr_off + g]);
+  const int s1 = __builtin_amdgcn_readfirstlane(a.plan[a.grp_ptr_off + g + 1]);
   const int ns = s1 - s0;
   if (ns == 1) return;
   const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (r >= a.R) return;
-  const int c = (threadIdx.x & 63) * 8;
+  const int lane = threadIdx.x & 63;
+  const int c = lane * 8;
 
   int b, t, h;
   if (a.sparse) {
@@ -45,22 +59,43 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     h = r % a.H;
   }
 
+  // the row's split weights: lane i holds split s0 + i of each 64-split chunk
   float mx = kNegInf;
-  for (int s = s0; s < s1; ++s) mx = fmaxf(mx, a.part_lse[(int64_t)s * a.R + r]);
+  for (int s = s0; s < s1; s += 64)
+    if (s + lane < s1) mx = fmaxf(mx, a.part_lse[(int64_t)(s + lane) * a.R + r]);
+  mx = wave_max(mx);
   float wsum = 0.f;
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   if (mx != kNegInf) {
-    for (int s = s0; s < s1; ++s) {
-      const float ls = a.part_lse[(int64_t)s * a.R + r];
-      const float w = (ls == kNegInf) ? 0.f : __expf(ls - mx);
-      wsum += w;
-      const float4* src = reinterpret_cast<const float4*>(a.part_o + ((int64_t)s * a.R + r) * kDv + c);
-      const float4 v0 = src[0], v1 = src[1];
-      acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
-      acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
+    for (int sc = s0; sc < s1; sc += 64) {
+      const float ls = (sc + lane < s1) ? a.part_lse[(int64_t)(sc + lane) * a.R + r] : kNegInf;
+      const float wl = (ls == kNegInf) ? 0.f : __expf(ls - mx);
+      wsum += wl;
+      const int nc = min(64, s1 - sc);
+      // four splits' rows in flight at a time
+      for (int k = 0; k < nc; k += 4) {
+        float4 v[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (k + q < nc) {
+            const float4* src = reinterpret_cast<const float4*>(a.part_o + ((int64_t)(sc + k + q) * a.R + r) * kDv + c);
+            v[q][0] = src[0];
+            v[q][1] = src[1];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (k + q < nc) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k + q));
+            acc[0] += w * v[q][0].x; acc[1] += w * v[q][0].y; acc[2] += w * v[q][0].z; acc[3] += w * v[q][0].w;
+            acc[4] += w * v[q][1].x; acc[5] += w * v[q][1].y; acc[6] += w * v[q][1].z; acc[7] += w * v[q][1].w;
+          }
+        }
+      }
     }
+    wsum = wave_sum(wsum);
   }
   float lse, scale;
   if (wsum > 0.f) {
@@ -88,7 +123,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   w.z = (uint32_t)f2bf(acc[4] * scale) | ((uint32_t)f2bf(acc[5] * scale) << 16);
   w.w = (uint32_t)f2bf(acc[6] * scale) | ((uint32_t)f2bf(acc[7] * scale) << 16);
   *reinterpret_cast<uint4*>(a.out + ((int64_t)g * a.R + r) * kDv + c) = w;
-  if ((threadIdx.x & 63) == 0) a.lse[((int64_t)b * a.H + h) * a.Sq + t] = lse;
+  if (lane == 0) a.lse[((int64_t)b * a.H + h) * a.Sq + t] = lse;
 }
 
 }  // namespace
