@@ -10,7 +10,7 @@
  *
  *   mla_decode_plan  per-query-group split and work-unit metadata, computed on the device
  *   mla_decode       paged gather, QK^T, online softmax, PV; final O/LSE for groups processed in
- *                    one piece, fp32 partials for the others
+ *                    one piece, split partials (bf16 O, fp32 LSE) for the others
  *   mla_combine      log-sum-exp merge of the partials (and the sink), final O/LSE
  *
  * Conventions shared by every call
@@ -80,8 +80,9 @@ typedef struct mla_problem {
 
 /* Buffer sizes for a problem planned over `num_cus` compute units (0: the current device's CU
  * count). plan_bytes (host out): the plan buffer for mla_decode_plan. partial_bytes (host out):
- * the fp32 split partials for mla_decode/mla_combine ([S_max][R][d_v] O then [S_max][R] LSE with
- * S_max = groups + units). Either output pointer may be NULL. */
+ * the split partials for mla_decode/mla_combine (bf16 [S_max][R][d_v] O, each split normalised by
+ * its own softmax sum, then fp32 [S_max][R] LSE, S_max = groups + units). Either output pointer
+ * may be NULL. */
 int mla_get_workspace_size(const mla_problem* p, int32_t num_cus, size_t* plan_bytes,
                            size_t* partial_bytes);
 
@@ -108,7 +109,7 @@ int mla_decode_plan(const mla_problem* p, int32_t num_cus, const int32_t* seqlen
  *               outside [0, seqlens[b]) are skipped, repeats count once per occurrence
  *   sink        fp32 [H] per-head sink logits added once to each softmax denominator, or NULL
  *   plan        from mla_decode_plan with the same problem and num_cus
- *   partials    fp32 workspace of at least the partial_bytes mla_get_workspace_size gives
+ *   partials    workspace of at least the partial_bytes mla_get_workspace_size gives
  *   out         bf16 [B, Sq, H, d_v]; lse fp32 [B, H, Sq] natural-log LSE of the scaled scores
  *               (sink included). Groups processed in one piece are written here; the rest are
  *               written by mla_combine, which must follow on the same stream. */

@@ -78,7 +78,8 @@ int derive(const mla_problem* p, int32_t num_cus, Shape* sh) {
 }
 
 size_t partial_size(const Shape& sh) {
-  return (size_t)sh.s_max * (size_t)sh.R * (size_t)(mla::kDv + 1) * sizeof(float);
+  // bf16 partial O rows, then fp32 partial LSEs
+  return (size_t)sh.s_max * (size_t)sh.R * ((size_t)mla::kDv * sizeof(uint16_t) + sizeof(float));
 }
 
 int launch_rc(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
@@ -156,8 +157,8 @@ int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void*
   a.sink = sink;
   a.plan = static_cast<const int32_t*>(plan);
   a.zero_row = static_cast<const uint8_t*>(plan) + lay.zero_row_bytes_off;
-  a.part_o = static_cast<float*>(partials);
-  a.part_lse = a.part_o + (size_t)sh.s_max * sh.R * mla::kDv;
+  a.part_o = static_cast<uint16_t*>(partials);
+  a.part_lse = reinterpret_cast<float*>(a.part_o + (size_t)sh.s_max * sh.R * mla::kDv);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.page_stride = sh.page_stride;
@@ -196,8 +197,8 @@ int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const v
   const PlanLayout lay = PlanLayout::make(sh.G, sh.U);
   mla::CombineArgs a;
   a.plan = static_cast<const int32_t*>(plan);
-  a.part_o = static_cast<const float*>(partials);
-  a.part_lse = a.part_o + (size_t)sh.s_max * sh.R * mla::kDv;
+  a.part_o = static_cast<const uint16_t*>(partials);
+  a.part_lse = reinterpret_cast<const float*>(a.part_o + (size_t)sh.s_max * sh.R * mla::kDv);
   a.sink = sink;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;

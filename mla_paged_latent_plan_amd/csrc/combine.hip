@@ -9,7 +9,7 @@
 // mla_decode and are skipped.
 //
 // Launch: one workgroup of 256 threads per (group, 4 query rows); 64 threads per row, each
-// owning 8 consecutive columns, so partial rows are read as contiguous 2 KB lines. Lane i reads
+// owning 8 consecutive columns, so bf16 partial rows are read as contiguous 1 KB lines. Lane i reads
 // the LSE of split i (per chunk of 64 splits); four splits' rows are loaded before they are
 // accumulated.
 #include "mla_internal.h"
@@ -76,21 +76,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       const int nc = min(64, s1 - sc);
       // four splits' rows in flight at a time
       for (int k = 0; k < nc; k += 4) {
-        float4 v[4][2];
+        uint4 v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          if (k + q < nc) {
-            const float4* src = reinterpret_cast<const float4*>(a.part_o + ((int64_t)(sc + k + q) * a.R + r) * kDv + c);
-            v[q][0] = src[0];
-            v[q][1] = src[1];
-          }
+          if (k + q < nc)
+            v[q] = *reinterpret_cast<const uint4*>(a.part_o + ((int64_t)(sc + k + q) * a.R + r) * kDv + c);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if (k + q < nc) {
             const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k + q));
-            acc[0] += w * v[q][0].x; acc[1] += w * v[q][0].y; acc[2] += w * v[q][0].z; acc[3] += w * v[q][0].w;
-            acc[4] += w * v[q][1].x; acc[5] += w * v[q][1].y; acc[6] += w * v[q][1].z; acc[7] += w * v[q][1].w;
+            const uint32_t u[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc[2 * i] += w * __uint_as_float(u[i] << 16);
+              acc[2 * i + 1] += w * __uint_as_float(u[i] & 0xFFFF0000u);
+            }
           }
         }
       }

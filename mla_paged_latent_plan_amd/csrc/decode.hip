@@ -3,8 +3,8 @@
 // What it computes (vLLM mla_attention.py module docstring, "Data-Movement Friendly Approach"):
 // all heads of a query group attend over the same latent rows, K = [kv_c, k_pe] (d_qk wide) and
 // V = kv_c (the first 512 columns). Per split (a run of 64-row blocks of one group, from the
-// plan) a workgroup produces either the final bf16 O and natural-log LSE, or an fp32 partial
-// (O normalised by its own denominator, LSE without the sink) for mla_combine.
+// plan) a workgroup produces either the final bf16 O and natural-log LSE, or a partial
+// (bf16 O normalised by its own denominator, fp32 LSE without the sink) for mla_combine.
 //
 // Mapping onto CDNA4:
 // - Workgroup = 4 waves; the group's query rows (heads, times tokens when q_len > 1) are the
@@ -552,10 +552,14 @@ struct Decoder {
       }
       if (gl == 0) a.lse[lse_index(r)] = lse_nat;
     } else {
-      float* dst = a.part_o + ((int64_t)s * a.R + r) * kDv + 4 * gl;
+      uint16_t* dst = a.part_o + ((int64_t)s * a.R + r) * kDv + 4 * gl;
 #pragma unroll
       for (int dt = 0; dt < kDv / 16; ++dt) {
-        *reinterpret_cast<f32x4*>(dst + 16 * dt) = orow[dt] * scale;
+        const f32x4 v = orow[dt] * scale;
+        uint2 w;
+        w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+        w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+        *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
         __builtin_amdgcn_sched_barrier(0);
       }
       if (gl == 0) a.part_lse[(int64_t)s * a.R + r] = lse_nat;
@@ -568,14 +572,14 @@ struct Decoder {
     float lse_nat, scale;
     row_norm(r, m2, l, final_out, &lse_nat, &scale);
     v *= scale;
+    uint2 w;
+    w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
     if (final_out) {
-      uint2 w;
-      w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-      w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
       *reinterpret_cast<uint2*>(a.out + ((int64_t)g * a.R + r) * kDv + col) = w;
       if (write_lse) a.lse[lse_index(r)] = lse_nat;
     } else {
-      *reinterpret_cast<f32x4*>(a.part_o + ((int64_t)s * a.R + r) * kDv + col) = v;
+      *reinterpret_cast<uint2*>(a.part_o + ((int64_t)s * a.R + r) * kDv + col) = w;
       if (write_lse) a.part_lse[(int64_t)s * a.R + r] = lse_nat;
     }
   }
@@ -1212,10 +1216,14 @@ struct Spec64 {
           }
           if (vw == 0 && gl == 0) a.lse[lse_index(r)] = lse_nat;
         } else {
-          float* dst = a.part_o + ((int64_t)s * a.R + r) * kDv + col0;
+          uint16_t* dst = a.part_o + ((int64_t)s * a.R + r) * kDv + col0;
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
-            *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt][ht] * scale;
+            const f32x4 v = o[dt][ht] * scale;
+            uint2 w;
+            w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+            w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+            *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
             __builtin_amdgcn_sched_barrier(0);
           }
           if (vw == 0 && gl == 0) a.part_lse[(int64_t)s * a.R + r] = lse_nat;

@@ -69,7 +69,7 @@ struct DecodeArgs {
   const float* sink;
   const int32_t* plan;
   const uint8_t* zero_row;
-  float* part_o;
+  uint16_t* part_o;  // bf16 [S_max][R][512] partial outputs, each normalised by its own sum
   float* part_lse;
   uint16_t* out;
   float* lse;
@@ -82,7 +82,7 @@ struct DecodeArgs {
 
 struct CombineArgs {
   const int32_t* plan;
-  const float* part_o;
+  const uint16_t* part_o;
   const float* part_lse;
   const float* sink;
   uint16_t* out;

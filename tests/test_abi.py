@@ -57,16 +57,16 @@ def test_workspace_sizes(lib):
     G, U = 2, 256
     words = 16 + (G + 1) + (U + 1) + 2 * G + 4 * (G + U)
     assert plan_b == ((words * 4 + 255) // 256) * 256 + 2048
-    assert part_b == (G + U) * 16 * 513 * 4
+    assert part_b == (G + U) * 16 * (512 * 2 + 4)
     # 128 heads: two 64-row tiles per group, U = cus / 2
     rc, _, part_b = ws(good(num_heads=128), 256)
-    assert rc == 0 and part_b == (2 + 128) * 128 * 513 * 4
+    assert rc == 0 and part_b == (2 + 128) * 128 * (512 * 2 + 4)
     # 4 tokens x 64 heads = 256 rows -> 4 tiles, U = 64
     rc, _, part_b = ws(good(num_heads=64, q_len=4, causal=1, window=128), 256)
-    assert rc == 0 and part_b == (2 + 64) * 256 * 513 * 4
+    assert rc == 0 and part_b == (2 + 64) * 256 * (512 * 2 + 4)
     # index lists: groups are (request, token) pairs of H rows
     rc, _, part_b = ws(good(num_heads=128, q_len=2, topk=64), 256)
-    assert rc == 0 and part_b == (4 + 128) * 128 * 513 * 4
+    assert rc == 0 and part_b == (4 + 128) * 128 * (512 * 2 + 4)
 
 
 @pytest.mark.parametrize("kw,status", [
