@@ -622,6 +622,28 @@ struct Decoder {
   }
 };
 
+// LDS-DMA as inline assembly (M0 = wave-uniform LDS base, one 16- or 4-byte element per lane).
+// Seeing the DMA builtin in a loop, the compiler's wait-count pass falls back to waiting for every
+// outstanding LDS read before each use; the kernels that use these helpers order their DMA and LDS
+// reads with explicit vmcnt waits and barriers instead. M0 has no other user in those kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_x4(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+// row (wave-uniform, scalar registers) + lane_off
+__device__ __forceinline__ void dma_x4s(uint32_t lane_off, uint64_t row, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(lane_off), "s"(row), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_x1(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(lds_ptr p) { return (uint32_t)(uintptr_t)p; }
+
 // Workgroup barrier for LDS hand-offs only: unlike __syncthreads() it does not wait for
 // outstanding global loads, so the next block's LDS-DMA stays in flight across it.
 __device__ __forceinline__ void lds_barrier() {
@@ -758,7 +780,7 @@ struct Spec64 {
   const DecodeArgs& a;
   lds_ptr sm;
   int lane, wave;
-  int g, b, L, j0, n, q0, qend, nsplit;
+  int g, b, L, j0, n, q0, qend, nsplit, cur_split;
 
   __device__ Spec64(const DecodeArgs& args, lds_ptr base) : a(args), sm(base) {
     lane = threadIdx.x & 63;
@@ -776,7 +798,7 @@ struct Spec64 {
   }
   __device__ __forceinline__ void dma_dword(const int32_t* src, uint32_t dst) const {
     if (lane < 8)
-      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + dst), 4, 0, 0);
+      dma_x1(src, lds_addr(sm + dst));
   }
   __device__ __forceinline__ int ri_read(uint32_t slot) const {
     return *reinterpret_cast<const LDS_AS int*>(sm + slot + 4 * (lane & 7));
@@ -827,16 +849,11 @@ struct Spec64 {
         const uint64_t rb = (lane < 32) ? b0 : b1;
         const int row = r0 + 2 * i + (lane >> 5);
         const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 16 * ((lane & 31) ^ swz_n(row));
-        __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + (r0 + 2 * i) * 512), 16, 0, 0);
+        dma_x4(src, lds_addr(sm + sa + (r0 + 2 * i) * 512));
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint64_t rb = readlane64(base, i);
-        const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 16 * lane;
-        __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + (r0 + i) * kRowStrideA),
-                                         16, 0, 0);
-      }
+      for (int i = 0; i < 8; ++i) dma_x4s(16 * lane, readlane64(base, i), lds_addr(sm + sa + (r0 + i) * kRowStrideA));
     }
     if constexpr (HAS_B) {
       const int r = r0 + (lane >> 3);
@@ -845,8 +862,7 @@ struct Spec64 {
       const uint32_t hi = __shfl((uint32_t)(base >> 32), lane >> 3, 64);
       const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo)) +
                            kRopeSrc + 16 * c;
-      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + kSlotA + (wave - 4) * 1024),
-                                       16, 0, 0);
+      dma_x4(src, lds_addr(sm + sa + kSlotA + (wave - 4) * 1024));
     }
     if constexpr (FP8) {
       // scale slots: 8 rows x 8 bytes, one dword per lane
@@ -856,13 +872,14 @@ struct Spec64 {
       // scale slots are 8-byte aligned: the dword offset is an OR into the low word
       const int32_t* src = reinterpret_cast<const int32_t*>((uintptr_t)(((uint64_t)hi << 32) | (lo | (4u * (lane & 1)))));
       if (lane < 16)
-        __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + kScOff + r0 * 8), 4, 0, 0);
+        dma_x1(src, lds_addr(sm + sa + kScOff + r0 * 8));
     }
     page_fetch(x + 3);
     if (a.topk > 0) idx_fetch(x + 6);
   }
 
   __device__ __forceinline__ void load_split(int s) {
+    cur_split = s;
     const int32_t* plan = a.plan;
     const int32_t* rec = plan + a.splits_off + 4 * (int64_t)s;
     // split-wide values, kept in scalar registers (uniform across the workgroup)
@@ -1031,7 +1048,27 @@ struct Spec64 {
       *reinterpret_cast<LDS_AS float*>(sm + kLOff + 256 + 4 * (wave * 16 + nl)) = m_ref;
     }
     lds_barrier();  // statistics published
-    lds_barrier();  // value waves done with the split's LDS
+    lds_barrier();  // output rows staged
+    store_rows(mt);
+    lds_barrier();  // staging area and slots reused by the next split
+  }
+
+  // Output rows of the tile leave LDS as whole 1 KB rows: wave w stores rows [8w, 8w + 8).
+  static constexpr int kStageRow = 1040;  // 16 bytes of padding spread the 8-byte staging writes
+  static_assert(64 * kStageRow <= 4 * kSlot, "output staging fits in the slots");
+  __device__ __forceinline__ void store_rows(int mt) {
+    const int s = cur_split;
+    const bool final_out = (nsplit == 1);
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int hrow = 8 * wave + rr;
+      const int r = mt * 64 + hrow;
+      if (r < a.R) {
+        const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(sm + hrow * kStageRow + 16 * lane);
+        uint16_t* dst = final_out ? a.out + ((int64_t)g * a.R + r) * kDv : a.part_o + ((int64_t)s * a.R + r) * kDv;
+        *reinterpret_cast<u32x4*>(dst + 8 * lane) = v;
+      }
+    }
   }
 
   // ===== value waves ===========================================================================
@@ -1190,7 +1227,8 @@ struct Spec64 {
     mfma_drain_acc(o);
     lds_barrier();  // score waves' statistics published
 
-    // ---- epilogue: each value wave writes its 128 columns of all 64 rows ---------------------
+    // ---- epilogue: each value wave normalises its 128 columns of all 64 rows into the staging
+    // rows (all slots are free: every bundle landed before the last barrier) ------------------
     const bool final_out = (nsplit == 1);
     const int tile0 = mt * 64;
 #pragma unroll
@@ -1199,38 +1237,24 @@ struct Spec64 {
       const int r = tile0 + hrow;
       const float lt = *reinterpret_cast<const LDS_AS float*>(sm + kLOff + 4 * hrow);
       const float m2 = *reinterpret_cast<const LDS_AS float*>(sm + kLOff + 256 + 4 * hrow);
-      if (r < a.R) {
-        float lse_nat, scale;
-        row_norm(r, m2, lt, final_out, &lse_nat, &scale);
-        const int col0 = 128 * vw + 4 * gl;
-        if (final_out) {
-          uint16_t* dst = a.out + ((int64_t)g * a.R + r) * kDv + col0;
+      float lse_nat, scale;
+      row_norm(min(r, a.R - 1), m2, lt, final_out, &lse_nat, &scale);
+      const uint32_t row_at = hrow * kStageRow + 2 * (128 * vw + 4 * gl);
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) {
-            const f32x4 v = o[dt][ht] * scale;
-            uint2 w;
-            w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-            w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-            *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          if (vw == 0 && gl == 0) a.lse[lse_index(r)] = lse_nat;
-        } else {
-          uint16_t* dst = a.part_o + ((int64_t)s * a.R + r) * kDv + col0;
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) {
-            const f32x4 v = o[dt][ht] * scale;
-            uint2 w;
-            w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-            w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-            *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          if (vw == 0 && gl == 0) a.part_lse[(int64_t)s * a.R + r] = lse_nat;
-        }
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 v = o[dt][ht] * scale;
+        const u32x2 w = {(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                         (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
+        *reinterpret_cast<LDS_AS u32x2*>(sm + row_at + 32 * dt) = w;
+      }
+      if (vw == 0 && gl == 0 && r < a.R) {
+        if (final_out) a.lse[lse_index(r)] = lse_nat;
+        else a.part_lse[(int64_t)s * a.R + r] = lse_nat;
       }
     }
-    lds_barrier();  // statistics buffer and slots reused by the next split
+    lds_barrier();  // output rows staged
+    store_rows(mt);
+    lds_barrier();  // staging area and slots reused by the next split
   }
 
   // LSE (natural log) and output scale of a row; the sink is folded in for final outputs.
