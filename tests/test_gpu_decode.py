@@ -33,6 +33,13 @@ CASES = {
     "d512_window_sink": (Spec("d512_window_sink", batch=4, q_len=4, num_heads=16, d_qk=512,
                               page_size=64, seqlens=(3, 131, 1000, 4), causal=True, window=128,
                               sink=True, sm_scale=1 / math.sqrt(512), seed=15), None),
+    # bf16 rows, d_qk 512 (no RoPE region) at 64-row tiles: 64 heads x 2 causal tokens
+    "d512_h64_sq2": (Spec("d512_h64_sq2", batch=3, q_len=2, num_heads=64, d_qk=512, page_size=64,
+                          seqlens=(2, 640, 97), causal=True, sm_scale=1 / math.sqrt(512), seed=19),
+                     None),
+    # 40 stacked rows: one 64-row tile with 24 padding rows
+    "h40_padded_tile": (Spec("h40_padded_tile", batch=3, q_len=1, num_heads=40, page_size=32,
+                             seqlens=(33, 1200, 64), sm_scale=S, seed=20), None),
     "sparse_h128": (Spec("sparse_h128", batch=2, q_len=1, num_heads=128, page_size=64,
                          seqlens=(5000, 3), topk=300, sm_scale=S, seed=16), None),
     "sparse_h16_lens": (Spec("sparse_h16_lens", batch=2, q_len=2, num_heads=16, page_size=16,
