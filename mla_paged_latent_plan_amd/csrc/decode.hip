@@ -20,7 +20,7 @@
 //   block). The S^T accumulator layout is directly the B operand of PV, so P never leaves
 //   registers; V^T comes from the transposed LDS read.
 // - Online softmax in base 2 with a lazily moved reference maximum: O is rescaled only when a
-//   row's maximum grows by more than 2^8, which keeps the 256 accumulator registers untouched in
+//   row's maximum grows by more than 2^16, which keeps the 256 accumulator registers untouched in
 //   the common case. Row statistics are per lane (the head index runs along lanes).
 // - Masked rows (past the group's rows, invalid indices, pages outside the cache) are gathered
 //   from the plan's zero row, so no NaN from unused cache bytes can reach the accumulators.
@@ -44,7 +44,10 @@ constexpr int kRowStrideA = 1056;            // latent part: 1 KB + 32 B padding
 constexpr int kStageA = kBlockRows * kRowStrideA;
 constexpr int kStageB = kBlockRows * 128;    // RoPE tails (64 bf16), XOR-swizzled
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kTau = 8.0f;                 // lazy rescale threshold (log2 units)
+// Lazy rescale threshold (log2 units): the reference maximum of a row moves, and O is rescaled, only
+// when the row maximum exceeds it by more than 2^16. Probabilities then stay below 2^16 (exact range
+// in bf16, relative rounding unchanged) and O below 2^16 x rows x max|V|, far inside fp32.
+constexpr float kTau = 16.0f;
 
 template <int HW_, int WN_, int DQK_>
 struct Cfg {
@@ -1111,10 +1114,14 @@ struct Spec64 {
         const int u = t - 1;  // step accumulated now
         const uint32_t pbo = (u & 1);
         const LDS_AS int* fl = reinterpret_cast<const LDS_AS int*>(sm + kFOff + pbo * 16);
-        if (fl[0] | fl[1] | fl[2] | fl[3]) {
+        const int f0 = fl[0], f1 = fl[1], f2 = fl[2], f3 = fl[3];
+        if (f0 | f1 | f2 | f3) {
+          // only the row tiles whose score wave moved its reference maximum (tile ht = wave ht)
           mfma_drain_acc(o);
 #pragma unroll
           for (int ht = 0; ht < 4; ++ht) {
+            const int f = (ht == 0) ? f0 : (ht == 1) ? f1 : (ht == 2) ? f2 : f3;
+            if (!f) continue;
             const float al = *reinterpret_cast<const LDS_AS float*>(sm + kAOff + pbo * 256 + 4 * (16 * ht + nl));
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
