@@ -64,8 +64,10 @@ struct Cfg {
   static constexpr int KS = DQK / 32;
   static constexpr bool HAS_B = DQK > 512;
   static constexpr int STAGE = kStageA + (HAS_B ? kStageB : 0);
-  static constexpr int LDS = 2 * STAGE;
-  static_assert(WN == 1 || 4 * HW * kDv * 4 + 8 * HW * 4 <= LDS,
+  static constexpr int RI_OFF = 2 * STAGE;  // row entries: block-table [4][64], index [8][64]
+  static constexpr int LDS = RI_OFF + 12 * 256;
+  static constexpr int NB = 16 + (HAS_B ? 2 : 0) + 1;  // memory instructions per dense bundle
+  static_assert(WN == 1 || 4 * HW * kDv * 4 + 8 * HW * 4 <= RI_OFF,
                 "merge scratch must fit in the stage buffers");
 };
 
@@ -160,11 +162,33 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
-// Per-lane row descriptor for one stage (lane = row within the 64-row block).
-struct RowInfo {
-  int j;       // logical position (dense) or index value (sparse)
-  int valid;
-};
+// LDS-DMA as inline assembly (M0 = wave-uniform LDS base, one 16- or 4-byte element per lane).
+// Seeing the DMA builtin in a loop, the compiler's wait-count pass falls back to waiting for every
+// outstanding LDS read before each use; the kernels that use these helpers order their DMA and LDS
+// reads with explicit vmcnt waits and barriers instead. M0 has no other user in those kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_x4(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+// row (wave-uniform, scalar registers) + lane_off
+__device__ __forceinline__ void dma_x4s(uint32_t lane_off, uint64_t row, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(lane_off), "s"(row), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_x1(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(lds_ptr p) { return (uint32_t)(uintptr_t)p; }
+
+// Workgroup barrier for LDS hand-offs only: unlike __syncthreads() it does not wait for
+// outstanding global loads, so the next block's LDS-DMA stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <class C>
 struct Decoder {
@@ -184,49 +208,60 @@ struct Decoder {
   __device__ __forceinline__ uint32_t stage_a(int st) const { return st * C::STAGE; }
   __device__ __forceinline__ uint32_t stage_b(int st) const { return st * C::STAGE + kStageA; }
 
-  // Position (and validity) of block row `lane` of block `blk`: loads the index for sparse.
-  __device__ __forceinline__ RowInfo row_pos(int blk) const {
-    RowInfo r;
-    const int k = blk * kBlockRows + lane;
-    r.valid = (blk < ke) && (k < n);
-    if (a.topk > 0) {
-      int idx = -1;
-      if (r.valid) idx = a.indices[(int64_t)g * a.topk + k];
-      r.j = idx;
-      r.valid = r.valid && idx >= 0 && idx < L;
-    } else {
-      r.j = j0 + k;
-    }
-    // rows past the block table's capacity are read as zeros instead of indexing past it
-    r.valid = r.valid && (r.j >> a.ps_log2) < a.max_pages;
-    return r;
+  // Row entries of block x travel by LDS-DMA into workgroup rings (block-table entries of four
+  // blocks, index entries of eight), so no register ever waits on an in-flight load. Wave w fetches
+  // the entries of rows [16w, 16w + 16); addresses are clamped and the values validated when used.
+  __device__ __forceinline__ uint32_t pg_slot(int x) const { return C::RI_OFF + (x & 3) * 256; }
+  __device__ __forceinline__ uint32_t ix_slot(int x) const { return C::RI_OFF + 1024 + (x & 7) * 256; }
+  __device__ __forceinline__ void dma_entry(const int32_t* src, uint32_t slot) const {
+    if (lane < 16) dma_x1(src, lds_addr(sm + slot + 64 * wave));
   }
-  __device__ __forceinline__ int row_page(const RowInfo& r) const {
-    int page = 0;
-    if (r.valid) page = a.block_table[(int64_t)b * a.max_pages + (r.j >> a.ps_log2)];
-    return page;
+  __device__ __forceinline__ int ri_read(uint32_t slot, int row) const {
+    return *reinterpret_cast<const LDS_AS int*>(sm + slot + 4 * row);
   }
-  __device__ __forceinline__ uint64_t row_base(const RowInfo& r, int page, int* valid) const {
-    const bool ok = r.valid && page >= 0 && (int64_t)page < a.num_pages;
+  __device__ __forceinline__ int erow() const { return (16 * wave + lane) & 63; }
+  __device__ __forceinline__ void idx_fetch(int x) const {
+    const int k = min(x * kBlockRows + erow(), a.topk - 1);
+    dma_entry(a.indices + (int64_t)g * a.topk + max(k, 0), ix_slot(x));
+  }
+  // logical position (dense) or index value (sparse) of row `row` of block x
+  __device__ __forceinline__ int row_j(int x, int row) const {
+    return (a.topk > 0) ? ri_read(ix_slot(x), row) : j0 + x * kBlockRows + row;
+  }
+  __device__ __forceinline__ void page_fetch(int x) const {
+    const int pi = min(max(row_j(x, erow()) >> a.ps_log2, 0), a.max_pages - 1);
+    dma_entry(a.block_table + (int64_t)b * a.max_pages + pi, pg_slot(x));
+  }
+  // Global address of row `lane` of block x; invalid rows read the zero row.
+  __device__ __forceinline__ uint64_t row_base(int x, int* valid) const {
+    const int j = row_j(x, lane);
+    const int page = ri_read(pg_slot(x), lane);
+    const int k = x * kBlockRows + lane;
+    bool ok = k < n && (j >> a.ps_log2) < a.max_pages;
+    if (a.topk > 0) ok = ok && j >= 0 && j < L;
+    ok = ok && page >= 0 && (int64_t)page < a.num_pages;
     *valid = ok;
     if (!ok) return (uint64_t)(uintptr_t)a.zero_row;
-    const int slot = r.j & ((1 << a.ps_log2) - 1);
+    const int slot = j & ((1 << a.ps_log2) - 1);
     return (uint64_t)(uintptr_t)(a.cache + (int64_t)page * a.page_stride + (int64_t)slot * a.row_bytes);
   }
 
-  // Issue the LDS-DMA of one 64-row block into stage `st`; `base` is this lane's row address.
-  __device__ __forceinline__ void issue_stage(int st, uint64_t base) const {
-    const uint32_t sa = stage_a(st);
+  // Bundle x: the LDS-DMA of block x into stage x & 1 (wave w moves rows [16w, 16w + 16)), the
+  // block-table entries of block x + 2 and, with index lists, the index entries of block x + 4.
+  // Every wave issues the same C::NB (+1 sparse) memory instructions, so "bundle x has landed" is an
+  // exact vmcnt. Returns the valid-row mask of block x.
+  __device__ __forceinline__ uint64_t bundle(int x) const {
+    int v;
+    const uint64_t base = row_base(x, &v);
+    const uint64_t vm = __ballot(v);
+    const uint32_t sa = stage_a(x & 1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = wave * 16 + i;
-      const uint64_t rb = readlane64(base, r);
-      const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 16 * lane;
-      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sa + r * kRowStrideA),
-                                       16, 0, 0);
+      dma_x4s(16 * lane, readlane64(base, r), lds_addr(sm + sa + r * kRowStrideA));
     }
     if constexpr (C::HAS_B) {
-      const uint32_t sb = stage_b(st);
+      const uint32_t sb = stage_b(x & 1);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int k = wave * 2 + kk;
@@ -234,12 +269,14 @@ struct Decoder {
         const int c = (lane & 7) ^ swz_b(r);
         const uint32_t lo = __shfl((uint32_t)base, r, 64);
         const uint32_t hi = __shfl((uint32_t)(base >> 32), r, 64);
-        const uint64_t rb = ((uint64_t)hi << 32) | lo;
-        const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)rb) + 1024 + 16 * c;
-        __builtin_amdgcn_global_load_lds(src, reinterpret_cast<LDS_AS void*>(sm + sb + k * 1024), 16,
-                                         0, 0);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo)) +
+                             1024 + 16 * c;
+        dma_x4(src, lds_addr(sm + sb + k * 1024));
       }
     }
+    page_fetch(x + 2);
+    if (a.topk > 0) idx_fetch(x + 4);
+    return vm;
   }
 
   __device__ void run_split(int s, int mt) {
@@ -291,31 +328,42 @@ struct Decoder {
       for (int dt = 0; dt < kDv / 16; ++dt) o[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- prologue: row info for kb (now), kb+1 (pages), kb+2 (positions) -----------------
-    RowInfo r0 = row_pos(kb);
-    int valid0;
-    uint64_t base0 = row_base(r0, row_page(r0), &valid0);
-    uint64_t vmask_next = __ballot(valid0);
-    issue_stage(0, base0);
-    RowInfo r1 = row_pos(kb + 1);
-    int page1 = row_page(r1);
-    RowInfo r2 = row_pos(kb + 2);
+    // ---- prologue: index entries of blocks kb..kb+3, block-table entries of kb, kb+1 (in flight
+    // together with the Q loads), then bundle kb
+    const bool sparse = a.topk > 0;
+    if (sparse) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) idx_fetch(kb + i);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+    }
+    page_fetch(kb);
+    page_fetch(kb + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    // The Q registers are complete here. Naming them in an asm statement makes the compiler place
+    // its own wait for the Q loads now, before any row transfer is in flight: its wait counts do
+    // not see the inline-assembly transfers, so a wait placed later would also wait for those.
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) asm volatile("" : "+v"(qr[nt][ks]));
+    uint64_t vmask_next = bundle(kb);
 
     const bool dense_mask = (a.topk == 0) && (a.causal || a.window > 0);
     for (int blk = kb; blk < ke; ++blk) {
-      const int cur = (blk - kb) & 1;
+      const int cur = blk & 1;
       const uint64_t vmask = vmask_next;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      // bundle blk + 1 goes into the stage of block blk - 1, released at the last barrier; then
+      // wait for this wave's bundle blk, and the barrier makes every wave's transfers visible
       if (blk + 1 < ke) {
-        int v1;
-        const uint64_t base1 = row_base(r1, page1, &v1);
-        vmask_next = __ballot(v1);
-        issue_stage(cur ^ 1, base1);
-        r1 = r2;
-        page1 = row_page(r1);
-        r2 = row_pos(blk + 3);
+        vmask_next = bundle(blk + 1);
+        if (sparse) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(C::NB + 1) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(C::NB) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
+      lds_barrier();
 
       const uint32_t sa = stage_a(cur);
       const uint32_t sb = stage_b(cur);
@@ -340,21 +388,24 @@ struct Decoder {
           const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
           return lds_read_b128(sm, sb + row * 128 + 16 * c);
         };
-        // one step of operands in flight ahead of the MFMAs that consume the previous one
-        bf16x8 ka[2][C::KT];
+        // D - 1 steps of operands in flight ahead of the MFMAs that consume the oldest
+        constexpr int D = 4;
+        bf16x8 ka[D][C::KT];
 #pragma unroll
-        for (int kt = 0; kt < C::KT; ++kt) ka[0][kt] = k_operand(kt, 0);
+        for (int i = 0; i < D - 1; ++i)
+#pragma unroll
+          for (int kt = 0; kt < C::KT; ++kt) ka[i][kt] = k_operand(kt, i);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          if (ks + 1 < C::KS) {
+          if (ks + D - 1 < C::KS) {
 #pragma unroll
-            for (int kt = 0; kt < C::KT; ++kt) ka[(ks + 1) & 1][kt] = k_operand(kt, ks + 1);
+            for (int kt = 0; kt < C::KT; ++kt) ka[(ks + D - 1) % D][kt] = k_operand(kt, ks + D - 1);
           }
 #pragma unroll
           for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt)
-              sacc[kt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kt], qr[nt][ks],
+              sacc[kt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks % D][kt], qr[nt][ks],
                                                                      sacc[kt][nt], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -446,32 +497,36 @@ struct Decoder {
             const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
             return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
           };
-          bf16x8 va[2];
-          va[0] = v_operand(0);
+          bf16x8 va[D];
+#pragma unroll
+          for (int i = 0; i < D - 1; ++i) va[i] = v_operand(i);
 #pragma unroll
           for (int dt = 0; dt < kDv / 16; ++dt) {
-            if (dt + 1 < kDv / 16) va[(dt + 1) & 1] = v_operand(dt + 1);
+            if (dt + D - 1 < kDv / 16) va[(dt + D - 1) % D] = v_operand(dt + D - 1);
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt)
-              o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt & 1], p8[nt], o[nt][dt],
+              o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt % D], p8[nt], o[nt][dt],
                                                                   0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
           }
         } else {
-          bf16x4 va[2];
-          va[0] = lds_read_tr(sm, vbase);
+          bf16x4 va[D];
+#pragma unroll
+          for (int i = 0; i < D - 1; ++i) va[i] = lds_read_tr(sm, vbase + 32 * i);
 #pragma unroll
           for (int dt = 0; dt < kDv / 16; ++dt) {
-            if (dt + 1 < kDv / 16) va[(dt + 1) & 1] = lds_read_tr(sm, vbase + 32 * (dt + 1));
+            if (dt + D - 1 < kDv / 16) va[(dt + D - 1) % D] = lds_read_tr(sm, vbase + 32 * (dt + D - 1));
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt)
-              o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt & 1], p4[nt], o[nt][dt],
+              o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt % D], p4[nt], o[nt][dt],
                                                                     0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
+      lds_barrier();  // every wave done with stage cur (bundle blk + 2 goes there)
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // nothing in flight (also for empty splits)
     __syncthreads();  // all waves done with the stage buffers (reused by the merge below)
 
     // ---- epilogue ----------------------------------------------------------------------------
@@ -625,33 +680,7 @@ struct Decoder {
   }
 };
 
-// LDS-DMA as inline assembly (M0 = wave-uniform LDS base, one 16- or 4-byte element per lane).
-// Seeing the DMA builtin in a loop, the compiler's wait-count pass falls back to waiting for every
-// outstanding LDS read before each use; the kernels that use these helpers order their DMA and LDS
-// reads with explicit vmcnt waits and barriers instead. M0 has no other user in those kernels.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_x4(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_addr) : "memory", "m0");
-}
-// row (wave-uniform, scalar registers) + lane_off
-__device__ __forceinline__ void dma_x4s(uint32_t lane_off, uint64_t row, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(lane_off), "s"(row), "s"(lds_addr) : "memory", "m0");
-}
-__device__ __forceinline__ void dma_x1(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(lds_addr) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ uint32_t lds_addr(lds_ptr p) { return (uint32_t)(uintptr_t)p; }
 
-// Workgroup barrier for LDS hand-offs only: unlike __syncthreads() it does not wait for
-// outstanding global loads, so the next block's LDS-DMA stays in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // MFMAs with pinned register classes. The compiler keeps accumulators of builtin MFMAs in AGPRs
 // but loop-carried values in VGPRs, copying every accumulator once per iteration; pinning S^T to
