@@ -6,7 +6,8 @@ Each timed step is preceded (outside its events) by a read-only sweep over a 1 G
 was written once at set-up: it evicts the KV cache's lines from the 256 MB Infinity Cache and
 leaves only clean lines there, so the decode reads the KV cache from HBM without also paying for
 the write-back of an evicting kernel's dirty lines (a write fill of the same size is kept as an
-option, --flush write). A warm back-to-back figure is reported separately. Prints one JSON line.
+option, --flush write). Warm back-to-back figures are reported separately, eager and as a replayed
+HIP graph of the same steps. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|1|3|4|5|s1|s4] [--no-cpu]
 """
@@ -227,12 +228,12 @@ def main():
         mla.mla_decode_plan(p, num_cus, seq, None if wl.topk_lens is None else
                             wl.topk_lens.to(dev), runner.plan, stream)
 
-    def decode():
+    def decode(st=None):
         mla.mla_decode(p, num_cus, q, cache, bt, seq, s.sm_scale, idx, sink, runner.plan,
-                       runner.partials, out, lse, stream)
+                       runner.partials, out, lse, st or stream)
 
-    def combine():
-        mla.mla_combine(p, num_cus, runner.plan, runner.partials, sink, out, lse, stream)
+    def combine(st=None):
+        mla.mla_combine(p, num_cus, runner.plan, runner.partials, sink, out, lse, st or stream)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     # plan (once per forward; timed on its own)
@@ -279,6 +280,24 @@ def main():
     wb.record(stream)
     torch.cuda.synchronize()
     warm_ms = wa.elapsed_time(wb) / K
+
+    # the same K steps captured once in a HIP graph and replayed (warm cache, no launch gaps)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=cap):
+        for _ in range(K):
+            decode(cap)
+            combine(cap)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ga, gb = ev(), ev()
+    ga.record(stream)
+    graph.replay()
+    gb.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = ga.elapsed_time(gb) / K
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -336,6 +355,7 @@ def main():
         "combine_ms": round(float(com_ms.mean()), 4),
         "plan_ms": round(plan_ms, 4),
         "warm_ms_per_step": round(warm_ms, 4),
+        "graph_warm_ms_per_step": round(graph_ms, 4),
         "wall_ms_per_step_with_flush": round(wall, 4),
         "cache_eviction": "none" if args.no_flush else
                           ("read-only 1 GiB sweep" if args.flush == "read" else "512 MB write fill"),

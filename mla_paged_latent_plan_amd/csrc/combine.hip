@@ -10,7 +10,7 @@
 //
 // Launch: one workgroup of 256 threads per (group, 4 query rows); 64 threads per row, each
 // owning 8 consecutive columns, so bf16 partial rows are read as contiguous 1 KB lines. Lane i reads
-// the LSE of split i (per chunk of 64 splits); four splits' rows are loaded before they are
+// the LSE of split i (per chunk of 64 splits); eight splits' rows are loaded before they are
 // accumulated.
 #include "mla_internal.h"
 
@@ -19,6 +19,7 @@ namespace mla {
 namespace {
 
 constexpr int kRowsPerBlock = 4;
+constexpr int kDepth = 8;  // partial rows in flight per lane
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
@@ -59,9 +60,23 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     h = r % a.H;
   }
 
-  // the row's split weights: lane i holds split s0 + i of each 64-split chunk
-  float mx = kNegInf;
-  for (int s = s0; s < s1; s += 64)
+  // The row's split weights: lane i holds split s0 + i of each 64-split chunk. The first chunk's
+  // LSEs and the first kDepth splits' rows are requested together, so a group with at most kDepth
+  // splits costs one memory round trip before its sums; larger groups then load kDepth rows at a
+  // time. Rows are accumulated in split order.
+  const int64_t row0 = (int64_t)r * kDv + c;
+  const uint16_t* po = a.part_o + (int64_t)s0 * a.R * kDv + row0;
+  const int64_t po_step = (int64_t)a.R * kDv;
+  // (indices past the group's last split repeat it: uniform, branch-free loads whose rows are
+  // not accumulated)
+  uint4 v[kDepth];
+  if (ns > 0) {
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q) v[q] = *reinterpret_cast<const uint4*>(po + min(q, ns - 1) * po_step);
+  }
+  float ls0 = (lane < ns) ? a.part_lse[(int64_t)(s0 + lane) * a.R + r] : kNegInf;
+  float mx = ls0;
+  for (int s = s0 + 64; s < s1; s += 64)
     if (s + lane < s1) mx = fmaxf(mx, a.part_lse[(int64_t)(s + lane) * a.R + r]);
   mx = wave_max(mx);
   float wsum = 0.f;
@@ -70,20 +85,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   if (mx != kNegInf) {
     for (int sc = s0; sc < s1; sc += 64) {
-      const float ls = (sc + lane < s1) ? a.part_lse[(int64_t)(sc + lane) * a.R + r] : kNegInf;
+      const float ls = (sc == s0) ? ls0
+                                  : (sc + lane < s1) ? a.part_lse[(int64_t)(sc + lane) * a.R + r] : kNegInf;
       const float wl = (ls == kNegInf) ? 0.f : __expf(ls - mx);
       wsum += wl;
       const int nc = min(64, s1 - sc);
-      // four splits' rows in flight at a time
-      for (int k = 0; k < nc; k += 4) {
-        uint4 v[4];
+      for (int k = 0; k < nc; k += kDepth) {
+        if (sc != s0 || k != 0) {  // the first kDepth rows are already loaded
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (k + q < nc)
-            v[q] = *reinterpret_cast<const uint4*>(a.part_o + ((int64_t)(sc + k + q) * a.R + r) * kDv + c);
+          for (int q = 0; q < kDepth; ++q)
+            v[q] = *reinterpret_cast<const uint4*>(po + (sc - s0 + min(k + q, nc - 1)) * po_step);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kDepth; ++q) {
           if (k + q < nc) {
             const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k + q));
             const uint32_t u[4] = {v[q].x, v[q].y, v[q].z, v[q].w};

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from workloads import CONFIGS, Spec, make
+from workloads import CONFIGS, SUPPLEMENTARY, Spec, make
 
 import mla_harness as H
 
@@ -160,10 +160,10 @@ def test_sparse_arange_equals_dense():
     assert m["max_abs"] <= 1e-2 and m["lse_max_abs"] <= 1e-4, m
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, "s1", "s4"])
 def test_full_size_configs(cfg):
     """The benchmark workloads at their full sizes, in the launch configuration the bench uses."""
-    wl = make(CONFIGS[cfg])
+    wl = make(SUPPLEMENTARY[cfg] if isinstance(cfg, str) else CONFIGS[cfg])
     print(f"[gpu] full-size config {cfg}", flush=True)
     out, lse, plan, used = H.run_gpu(wl)
     O, L, A = H.oracle_of(wl, abs_mass=True)
@@ -172,3 +172,40 @@ def test_full_size_configs(cfg):
     H.assert_parity(m, ctx=f"config {cfg}")
     want = H.plan_words(wl, used)
     assert np.array_equal(plan.view(torch.int32).numpy()[:len(want)], want)
+
+
+def test_graph_replay_matches_eager():
+    """decode + combine captured in a HIP graph: every replay equals the eager result bitwise.
+
+    Between replays the program does eager work of its own (the outputs are overwritten and the
+    device synchronised), so a replay that depended on state left by the capture would show."""
+    import mla_paged_latent_plan_amd as mla
+    wl = _make("fp8_h128_edges")  # multi-split groups: decode partials, then the combine merge
+    dev = H.to_device(wl)
+    p = H.problem_of(wl, mla)
+    runner = mla.MLADecode(p)
+    s = wl.spec
+    out = torch.empty(s.batch, s.q_len, s.num_heads, s.d_v, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(s.batch, s.num_heads, s.q_len, dtype=torch.float32, device="cuda")
+    runner.plan_(dev.seqlens, dev.topk_lens)
+    print("[gpu] graph replay: eager", flush=True)
+    runner.decode_(dev.q, dev.cache, dev.block_table, dev.seqlens, s.sm_scale, out, lse,
+                   indices=dev.indices, sink=dev.sink)
+    torch.cuda.synchronize()
+    o_ref, l_ref = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        runner.decode_(dev.q, dev.cache, dev.block_table, dev.seqlens, s.sm_scale, out, lse,
+                       indices=dev.indices, sink=dev.sink, stream=cap)
+    torch.cuda.synchronize()
+    for k in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        torch.cuda.synchronize()
+        print(f"[gpu] graph replay {k}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16)), f"replay {k}: out"
+        assert torch.equal(lse, l_ref), f"replay {k}: lse"
