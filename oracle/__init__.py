@@ -13,6 +13,7 @@ Everything is computed in float64 with numpy on dense, unpaged rows:
 - mha.py       the expanded (MHA-form) computation, used only to pin the absorbed form
 - paging.py    reads a paged cache back into dense rows
 - plan.py      the split/work-unit plan, integer arithmetic
+- kvwrite.py   writing new tokens' rows into the paged cache (bf16 copy, fp8 quantisation)
 
 Parity status of each function is stated in its module docstring.
 """
