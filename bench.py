@@ -38,7 +38,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="2")
+    ap.add_argument("--config", default=None,
+                    help="workload: 2 (default for decode), 1, 3 (default for kv_write), 4, 5, s1, s4")
+    ap.add_argument("--op", choices=("decode", "kv_write"), default="decode",
+                    help="decode: mla_decode + mla_combine (the default); kv_write: mla_kv_write "
+                         "of every row of the workload's requests in one launch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -113,10 +117,10 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per decode launch from the committed counter summary (FETCH_SIZE and WRITE_SIZE
-    runs, scaled by a plain copy's readings), if the kernel sources are unchanged since."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload_name}_hbm_counters.md")
+def measured_traffic(workload_name, kernel="decode"):
+    """HBM bytes per launch of the kernel from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE runs, scaled by a plain copy's readings), if the kernel sources are unchanged since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_name}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -187,17 +191,126 @@ def cpu_baseline(wl, target_s):
                        f"workload, float64 numpy oracle, {dt:.1f} s")
 
 
+def cpu_kv_write(kv_c, k_pe, fmt, target_s):
+    """The cache-write oracle, as it stands, on the first rows of the same inputs."""
+    from oracle import kvwrite
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < target_s and n < kv_c.shape[0]:
+        kvwrite.encode_row(kv_c[n], k_pe[n], fmt)
+        n += 1
+    dt = time.perf_counter() - t0
+    return dict(value=round(n / dt, 1), unit="rows/s", cores=1, kind="oracle",
+                sample=f"the first {n} rows of the same inputs, float64 numpy/python oracle "
+                       f"(oracle/kvwrite.py encode_row), one thread, {dt:.1f} s")
+
+
+def bench_kv_write(args):
+    """mla_kv_write of every row of the workload's requests (in request order through the block
+    table) in one launch: the cache write a prefill of these contexts would do."""
+    import torch
+    import mla_paged_latent_plan_amd as mla
+    from workloads import make
+    from workloads.gen import cache_layout
+
+    s = get_spec(args.config or "3")
+    wl = make(s)
+    dev = torch.device("cuda:0")
+    lay = cache_layout(s.kv_format, s.d_qk, s.d_rope, s.page_size)
+    bt = wl.block_table.numpy()
+    L = np.maximum(wl.seqlens.astype(np.int64), 0)
+    req = np.repeat(np.arange(s.batch), L)
+    pos = np.concatenate([np.arange(x) for x in L])
+    slots = bt[req, pos // s.page_size].astype(np.int64) * s.page_size + pos % s.page_size
+    n = len(slots)
+    g = torch.Generator().manual_seed(s.seed + 500)
+    kv_c_h = torch.randn(n, s.d_qk - s.d_rope, generator=g).to(torch.bfloat16)
+    k_pe_h = torch.randn(n, s.d_rope, generator=g).to(torch.bfloat16)
+    p = mla.make_problem(s.batch, s.q_len, s.num_heads, s.d_qk,
+                         mla.MLA_KV_BF16 if s.kv_format == "bf16" else mla.MLA_KV_FP8,
+                         s.page_size, wl.page_stride, wl.num_pages, int(bt.shape[1]))
+    kv_c, k_pe = kv_c_h.to(dev), k_pe_h.to(dev)
+    slot_d = torch.from_numpy(slots).to(dev)
+    cache = wl.cache.to(dev)
+    stream = torch.cuda.current_stream()
+    sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sweep_out = torch.empty(1, dtype=torch.float32, device=dev)
+    write = lambda: mla.mla_kv_write(p, kv_c, k_pe, slot_d, cache, stream)
+    for _ in range(args.warmup):
+        write()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(ev(), ev()) for _ in range(K)]
+    for k in range(K):
+        if not args.no_flush:
+            torch.sum(sweep, dim=0, out=sweep_out[0])
+        a, b = evs[k]
+        a.record(stream)
+        write()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    # context: a plain device-to-device copy of the rows' input bytes (read + write) after the
+    # same eviction, the rate a pure streaming kernel reaches on this GPU
+    src = torch.empty(n * 2 * s.d_qk, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    cms = []
+    for _ in range(5):
+        torch.sum(sweep, dim=0, out=sweep_out[0])
+        a, b = ev(), ev()
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        cms.append(a.elapsed_time(b))
+    copy_gbs = 2 * src.numel() / (float(np.median(cms)) / 1e3) / 1e9
+    del src, dst
+    out_row = lay["row_bytes"] + (8 if s.kv_format == "fp8" else 0)
+    alg_bytes = n * (2 * s.d_qk + out_row + 8)
+    t = float(ms.mean()) / 1e3
+    gbs = alg_bytes / t / 1e9
+    res = {
+        "metric": "MLA cache write: rows/s, achieved HBM GB/s, % of roofline",
+        "value": round(n / t, 1), "unit": "rows/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->" + ("bf16" if s.kv_format == "bf16" else "fp8-e4m3/ue8m0"),
+        "data": "synthetic",
+        "config": {"workload": f"kv_write {s.name}: {n} rows of d_qk {s.d_qk} written into pages of "
+                               f"{s.page_size} ({s.kv_format} rows of {lay['row_bytes']} B)",
+                   "rows": n, "parallelism": "single-gpu"},
+        "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4),
+                         traffic=measured_traffic(s.name, "kvwrite")),
+        "ms_p10_p90": [round(float(np.percentile(ms, 10)), 4),
+                       round(float(np.percentile(ms, 90)), 4)],
+        "algorithmic_bytes": int(alg_bytes),
+        "device_copy_gbs": round(copy_gbs, 1),
+        "cache_eviction": "none" if args.no_flush else "read-only 1 GiB sweep",
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu:
+        m = min(n, 20000)  # the oracle is timed on a bounded prefix of the rows
+        res["cpu_baseline"] = cpu_kv_write(kv_c_h[:m].to(torch.float64).numpy(),
+                                           k_pe_h[:m].to(torch.float64).numpy(), s.kv_format,
+                                           args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, "
-              "'How the path would shard'); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
+    if args.op == "kv_write":
+        return bench_kv_write(args)
     import torch
     import mla_paged_latent_plan_amd as mla
     from workloads import make
 
-    spec = get_spec(args.config)
+    spec = get_spec(args.config or "2")
     wl = make(spec)
     dev = torch.device("cuda:0")
     s = spec

@@ -13,6 +13,11 @@
  *                    one piece, split partials (bf16 O, fp32 LSE) for the others
  *   mla_combine      log-sum-exp merge of the partials (and the sink), final O/LSE
  *
+ * and, before them in a layer, the write of the new tokens' rows into the cache:
+ *
+ *   mla_kv_write     each new token's [kv_c, k_pe] row written in place into its cache slot,
+ *                    quantised to the fp8 row format when the cache holds fp8 rows
+ *
  * Conventions shared by every call
  * - All pointers are device pointers unless a parameter says "host". The caller owns every buffer;
  *   the library never allocates, frees or synchronises. `stream` is a hipStream_t (NULL = default
@@ -123,6 +128,24 @@ int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void*
  * then the sink; a group with no rows gets O = 0 and LSE = -inf (or LSE = sink_h). */
 int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const void* partials,
                 size_t partial_bytes, const float* sink, void* out, float* lse, void* stream);
+
+/* Cache write (vLLM mla_attention.py update_kv_cache(kv_c_normed, k_pe, kv_cache, slot_mapping,
+ * ...); HALOps MLA API, mla_attention kv_cache: each token's new row is written in place).
+ *   num_tokens   n >= 0 rows to write (0 enqueues nothing)
+ *   kv_c         bf16 [n, d_qk - d_rope], contiguous: the latent (NoPE) part of each row
+ *   k_pe         bf16 [n, d_rope], contiguous: the RoPE part (already rotated)
+ *   slot_mapping int64 [n], 8-byte aligned: slot = physical page * page_size + row in the page;
+ *                entries < 0 or >= num_pages * page_size are skipped. Slots must be distinct (two
+ *                rows for one slot: which lands is unspecified).
+ *   kv_cache     the paged cache in p->kv_format, p->page_stride_bytes, p->num_pages
+ * Only the dims, format and page fields of p are used (the rest must still be valid).
+ * bf16 rows are stored as given. fp8 rows: per 64-value group of kv_c, the ue8m0 scale byte is
+ * 127 + k for the smallest integer k with max|x| <= 448 * 2^k (k clamped to [-127, 127]; 127 for an
+ * all-zero group), and each code is x * 2^-k rounded to the nearest e4m3fn value, ties to even;
+ * k_pe is stored as bf16; unused bytes of the row's 8-byte scale slot are written as zero. Inputs
+ * must be finite. Other rows of the cache are not touched. */
+int mla_kv_write(const mla_problem* p, int64_t num_tokens, const void* kv_c, const void* k_pe,
+                 const int64_t* slot_mapping, void* kv_cache, void* stream);
 
 /* Static description of a status code. */
 const char* mla_strerror(int status);

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import MLA_KV_BF16, MLA_KV_FP8, MLAError, Problem  # noqa: F401
 
 __all__ = ["Problem", "make_problem", "workspace_size", "mla_decode_plan", "mla_decode",
-           "mla_combine", "MLADecode", "device_num_cus", "MLAError"]
+           "mla_combine", "mla_kv_write", "MLADecode", "device_num_cus", "MLAError"]
 
 
 def device_num_cus() -> int:
@@ -98,6 +98,26 @@ def mla_combine(p: Problem, num_cus: int, plan: torch.Tensor, partials: torch.Te
         p, num_cus, _ptr(plan, torch.uint8, "plan"), _ptr(partials, torch.uint8, "partials"),
         partials.numel(), _ptr(sink, torch.float32, "sink", p.num_heads),
         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def mla_kv_write(p: Problem, kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor,
+                 kv_cache: torch.Tensor, stream=None) -> None:
+    """Write each token's [kv_c, k_pe] row into its cache slot (fp8 caches: quantised)."""
+    lib = _lib.load()
+    n = int(kv_c.shape[0]) if kv_c.dim() == 2 else -1
+    if tuple(kv_c.shape) != (n, p.d_qk - p.d_rope):
+        raise ValueError(f"kv_c must be [n, {p.d_qk - p.d_rope}], got {tuple(kv_c.shape)}")
+    if tuple(k_pe.shape) != (n, p.d_rope):
+        raise ValueError(f"k_pe must be [{n}, {p.d_rope}], got {tuple(k_pe.shape)}")
+    if tuple(slot_mapping.shape) != (n,):
+        raise ValueError(f"slot_mapping must be [{n}], got {tuple(slot_mapping.shape)}")
+    if kv_cache.numel() * kv_cache.element_size() < p.num_pages * p.page_stride_bytes:
+        raise ValueError("kv_cache is smaller than num_pages * page_stride_bytes")
+    if not kv_cache.is_contiguous() or not kv_cache.is_cuda:
+        raise ValueError("kv_cache must be a contiguous device tensor")
+    _lib.check("mla_kv_write", lib.mla_kv_write(
+        p, n, _ptr(kv_c, torch.bfloat16, "kv_c"), _ptr(k_pe, torch.bfloat16, "k_pe"),
+        _ptr(slot_mapping, torch.int64, "slot_mapping"), kv_cache.data_ptr(), _stream(stream)))
 
 
 class MLADecode:

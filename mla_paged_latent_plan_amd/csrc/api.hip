@@ -212,6 +212,31 @@ int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const v
   return launch_rc(mla::launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 
+int mla_kv_write(const mla_problem* p, int64_t num_tokens, const void* kv_c, const void* k_pe,
+                 const int64_t* slot_mapping, void* kv_cache, void* stream) {
+  Shape sh;
+  int rc = derive(p, 1, &sh);
+  if (rc != MLA_OK) return rc;
+  if (num_tokens < 0 || num_tokens > (int64_t)INT32_MAX) return MLA_ERR_SHAPE;
+  if (num_tokens == 0) return MLA_OK;
+  if (kv_c == nullptr || k_pe == nullptr || slot_mapping == nullptr || kv_cache == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned16(kv_c) || !aligned16(k_pe) || !aligned16(kv_cache) ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
+    return MLA_ERR_ALIGN;
+  mla::KvWriteArgs a;
+  a.kv_c = static_cast<const uint16_t*>(kv_c);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.slots = slot_mapping;
+  a.cache = static_cast<uint8_t*>(kv_cache);
+  a.n = num_tokens;
+  a.num_slots = sh.num_pages * (int64_t)sh.page_size;
+  a.page_stride = sh.page_stride;
+  a.scale_off = (int64_t)sh.page_size * sh.row_bytes;
+  a.ps_log2 = sh.ps_log2;
+  return launch_rc(mla::launch_kv_write(a, sh.fmt, sh.d_qk - sh.d_rope,
+                                        static_cast<hipStream_t>(stream)));
+}
 const char* mla_strerror(int status) {
   switch (status) {
     case MLA_OK: return "ok";

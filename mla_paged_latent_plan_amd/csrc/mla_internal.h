@@ -1,4 +1,5 @@
-// Internal definitions shared by the plan, decode and combine kernels and the C-ABI layer.
+// Internal definitions shared by the plan, decode, combine and cache-write kernels and the C-ABI
+// layer.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -92,9 +93,20 @@ struct CombineArgs {
   int sparse;
 };
 
+struct KvWriteArgs {
+  const uint16_t* kv_c;  // bf16 [n][d_nope]
+  const uint16_t* k_pe;  // bf16 [n][64]
+  const int64_t* slots;  // [n]
+  uint8_t* cache;
+  int64_t n, num_slots, page_stride;
+  int64_t scale_off;  // fp8 rows: byte offset of a page's scale slots (page_size * row_bytes)
+  int ps_log2;
+};
+
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, const Shape& sh, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_kv_write(const KvWriteArgs& a, int fmt, int d_nope, hipStream_t s);
 
 }  // namespace mla

@@ -119,3 +119,24 @@ def test_host_checks_before_launch(lib):
     assert lib.mla_combine(ctypes.byref(p), 256, vp(4096), vp(4096), 1 << 30, None, None, vp(4096),
                            None) == 1
     assert lib.mla_strerror(6) == b"workspace buffer too small"
+
+
+def test_kv_write_host_checks(lib):
+    p = good()
+    vp = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    # no tokens: nothing to check or enqueue
+    assert lib.mla_kv_write(ctypes.byref(p), i64(0), None, None, None, None, None) == 0
+    assert lib.mla_kv_write(ctypes.byref(p), i64(-1), vp(4096), vp(4096), vp(4096), vp(4096),
+                            None) == 2
+    assert lib.mla_kv_write(ctypes.byref(p), i64(4), None, vp(4096), vp(4096), vp(4096), None) == 1
+    assert lib.mla_kv_write(ctypes.byref(p), i64(4), vp(4096), vp(4096), None, vp(4096), None) == 1
+    # misaligned rows, misaligned slot mapping
+    assert lib.mla_kv_write(ctypes.byref(p), i64(4), vp(4100), vp(4096), vp(4096), vp(4096),
+                            None) == 7
+    assert lib.mla_kv_write(ctypes.byref(p), i64(4), vp(4096), vp(4096), vp(4100), vp(4096),
+                            None) == 7
+    # an invalid problem is rejected first
+    bad = good(page_size=24)
+    assert lib.mla_kv_write(ctypes.byref(bad), i64(4), vp(4096), vp(4096), vp(4096), vp(4096),
+                            None) == 4
