@@ -109,9 +109,17 @@ def algorithmic(wl):
                 kv_rows=int(kv_rows), visible_pairs=int(vis))
 
 
-def source_hash():
+# Sources whose change invalidates a kernel's committed HBM counter readings: the kernel itself,
+# the shared argument/plan layout and, for decode, the plan (it decides the splits and partials).
+KERNEL_SOURCES = {
+    "decode": ("decode.hip", "plan.hip", "mla_internal.h"),
+    "kvwrite": ("kvwrite.hip", "mla_internal.h"),
+}
+
+
+def source_hash(kernel="decode"):
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.dirname(DECODE_SRC))):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(os.path.dirname(DECODE_SRC), f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -129,7 +137,7 @@ def measured_traffic(workload_name, kernel="decode"):
             m = re.match(r"- (source_hash|hbm_bytes_per_launch): (\S+)", line.strip())
             if m:
                 fields[m.group(1)] = m.group(2)
-    if fields.get("source_hash") != source_hash() or "hbm_bytes_per_launch" not in fields:
+    if fields.get("source_hash") != source_hash(kernel) or "hbm_bytes_per_launch" not in fields:
         return None
     return int(fields["hbm_bytes_per_launch"])
 
@@ -288,7 +296,7 @@ def bench_kv_write(args):
         "algorithmic_bytes": int(alg_bytes),
         "device_copy_gbs": round(copy_gbs, 1),
         "cache_eviction": "none" if args.no_flush else "read-only 1 GiB sweep",
-        "source_hash": source_hash(),
+        "source_hash": source_hash("kvwrite"),
     }
     if not args.no_cpu:
         m = min(n, 20000)  # the oracle is timed on a bounded prefix of the rows

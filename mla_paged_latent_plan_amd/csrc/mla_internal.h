@@ -41,9 +41,9 @@ struct PlanLayout {
 
 // Kernel tile for R stacked query rows per group: (M_TILE, FIXED split overhead in blocks).
 inline void tile_params(int R, int* m_tile, int* fixed) {
-  if (R <= 16) { *m_tile = 16; *fixed = 1; }
+  if (R <= 16) { *m_tile = 16; *fixed = 3; }
   else if (R <= 32) { *m_tile = 32; *fixed = 2; }
-  else { *m_tile = 64; *fixed = 2; }
+  else { *m_tile = 64; *fixed = 4; }
 }
 
 struct Shape {  // derived, validated problem shape
