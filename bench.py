@@ -40,9 +40,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=None,
                     help="workload: 2 (default for decode), 1, 3 (default for kv_write), 4, 5, s1, s4")
-    ap.add_argument("--op", choices=("decode", "kv_write"), default="decode",
+    ap.add_argument("--op", choices=("decode", "kv_write", "absorb"), default="decode",
                     help="decode: mla_decode + mla_combine (the default); kv_write: mla_kv_write "
-                         "of every row of the workload's requests in one launch")
+                         "of every row of the workload's requests in one launch; absorb: "
+                         "mla_q_absorb + mla_v_up for --tokens query tokens (DeepSeek-V3 dims)")
+    ap.add_argument("--tokens", type=int, default=64,
+                    help="absorb: query tokens (64 = the dsv3 decode batch)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -306,6 +309,93 @@ def bench_kv_write(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_absorb(args):
+    """mla_q_absorb then mla_v_up for T query tokens of DeepSeek-V3 shape (128 heads, P 128,
+    L 512, R 64, V 128): the per-head GEMMs on either side of the decode."""
+    import torch
+    import mla_paged_latent_plan_amd as mla
+    T, Hh, P, L, R, V = args.tokens, 128, 128, 512, 64, 128
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(2000 + T)
+    mk = lambda *sh, sc=1.0: (torch.randn(*sh, generator=g) * sc).to(torch.bfloat16).to(dev)
+    q_nope, q_pe = mk(T, Hh, P), mk(T, Hh, R)
+    w_uk, w_uv = mk(Hh, L, P, sc=P ** -0.5), mk(Hh, V, L, sc=L ** -0.5)
+    o = mk(T, Hh, L)
+    q_out = torch.empty(T, Hh, L + R, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(T, Hh, V, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sweep_out = torch.empty(1, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        mla.mla_q_absorb(q_nope, q_pe, w_uk, q_out, stream)
+        mla.mla_v_up(o, w_uv, out, stream)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(ev(), ev(), ev()) for _ in range(K)]
+    for k in range(K):
+        if not args.no_flush:
+            torch.sum(sweep, dim=0, out=sweep_out[0])
+        a, m, e = evs[k]
+        a.record(stream)
+        mla.mla_q_absorb(q_nope, q_pe, w_uk, q_out, stream)
+        m.record(stream)
+        mla.mla_v_up(o, w_uv, out, stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    qa = np.array([a.elapsed_time(m) for a, m, _ in evs])
+    vu = np.array([m.elapsed_time(e) for _, m, e in evs])
+    qa_bytes = 2 * (T * Hh * P + T * Hh * R + Hh * L * P + T * Hh * (L + R))
+    vu_bytes = 2 * (T * Hh * L + Hh * V * L + T * Hh * V)
+    flops = 2.0 * T * Hh * L * (P + V)
+    t = float((qa + vu).mean()) / 1e3
+    gbs = (qa_bytes + vu_bytes) / t / 1e9
+    bound = "hbm" if flops / (qa_bytes + vu_bytes) < MFMA_BF16_PEAK_TFS / HBM_PEAK_GBS * 1e3 else "mfma"
+    roof = (dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                 frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None) if bound == "hbm" else
+            dict(bound="mfma", achieved=round(flops / t / 1e12, 2), peak=MFMA_BF16_PEAK_TFS,
+                 unit="TFLOP/s", frac=round(flops / t / 1e12 / MFMA_BF16_PEAK_TFS, 4), traffic=None))
+    res = {
+        "metric": "MLA absorption GEMMs: query tokens/s, achieved HBM GB/s, % of roofline",
+        "value": round(T / t, 1), "unit": "query tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(float((qa + vu).mean()), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"absorb: {T} query tokens x {Hh} heads, W_UK [{Hh},{L},{P}], "
+                               f"W_UV [{Hh},{V},{L}], RoPE {R}", "tokens": T,
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "q_absorb_ms": round(float(qa.mean()), 4), "v_up_ms": round(float(vu.mean()), 4),
+        "q_absorb_gbs": round(qa_bytes / (float(qa.mean()) / 1e3) / 1e9, 1),
+        "v_up_gbs": round(vu_bytes / (float(vu.mean()) / 1e3) / 1e9, 1),
+        "algorithmic_bytes": int(qa_bytes + vu_bytes), "algorithmic_flops": flops,
+        "cache_eviction": "none" if args.no_flush else "read-only 1 GiB sweep",
+    }
+    if not args.no_cpu:
+        from oracle import absorb
+        t0 = time.perf_counter()
+        n = 0
+        qn = q_nope.cpu().to(torch.float64).numpy()
+        wk = w_uk.cpu().to(torch.float64).numpy()
+        oo = o.cpu().to(torch.float64).numpy()
+        wv = w_uv.cpu().to(torch.float64).numpy()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            absorb.q_absorb(qn, wk)
+            absorb.v_up(oo, wv)
+            n += 1
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = os.cpu_count() or 1
+        res["cpu_baseline"] = dict(value=round(n * T / dt, 1), unit="query tokens/s",
+                                   cores=threads, kind="oracle",
+                                   sample=f"{n} pass(es) over all {T} tokens, float64 numpy oracle "
+                                          f"(oracle/absorb.py), {dt:.1f} s")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -314,6 +404,8 @@ def main():
         sys.exit(2)
     if args.op == "kv_write":
         return bench_kv_write(args)
+    if args.op == "absorb":
+        return bench_absorb(args)
     import torch
     import mla_paged_latent_plan_amd as mla
     from workloads import make

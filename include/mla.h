@@ -18,6 +18,11 @@
  *   mla_kv_write     each new token's [kv_c, k_pe] row written in place into its cache slot,
  *                    quantised to the fp8 row format when the cache holds fp8 rows
  *
+ * and the per-head weight absorption on either side of the decode:
+ *
+ *   mla_q_absorb     the decode's query [q_nope x W_UK, q_pe] from the per-head query parts
+ *   mla_v_up         the per-head output o x W_UV from the decode's latent output
+ *
  * Conventions shared by every call
  * - All pointers are device pointers unless a parameter says "host". The caller owns every buffer;
  *   the library never allocates, frees or synchronises. `stream` is a hipStream_t (NULL = default
@@ -146,6 +151,31 @@ int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const v
  * must be finite. Other rows of the cache are not touched. */
 int mla_kv_write(const mla_problem* p, int64_t num_tokens, const void* kv_c, const void* k_pe,
                  const int64_t* slot_mapping, void* kv_cache, void* stream);
+
+/* Query absorption (vLLM mla_attention.py forward_mqa: ql_nope = q_nope x W_UK_T per head; module
+ * docstring, "Data-Movement Friendly Approach"), fused with assembling the decode's query:
+ *   q_out[t, h, 0:d_latent]              = sum_p q_nope[t, h, p] * w_uk[h, l, p]
+ *   q_out[t, h, d_latent:d_latent+d_rope] = q_pe[t, h, :]
+ *   tokens  T >= 0 query tokens (B * Sq of the decode; 0 enqueues nothing)
+ *   q_nope  bf16 [T, H, d_nope]; d_nope a multiple of 32 (128 for DeepSeek-V3)
+ *   q_pe    bf16 [T, H, d_rope] (already rotated), or NULL when d_rope = 0; d_rope a multiple of 8
+ *   w_uk    bf16 [H, d_latent, d_nope]: per head, each latent column's d_nope weights contiguous
+ *           (w_uk[h, l, p] = W_UK[l, h, p] of the (L, N, P) weight); d_latent a multiple of 64
+ *   q_out   bf16 [T, H, d_latent + d_rope]: the q argument of mla_decode when T = B * Sq
+ * All pointers 16-byte aligned. bf16 inputs, fp32 accumulation, bf16 output rounded to nearest even. */
+int mla_q_absorb(int32_t tokens, int32_t num_heads, int32_t d_nope, int32_t d_latent,
+                 int32_t d_rope, const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
+                 void* stream);
+
+/* Value up-projection (vLLM mla_attention.py _v_up_proj: (N, B, L) x (N, L, V) per head):
+ *   out[t, h, v] = sum_l o[t, h, l] * w_uv[h, v, l]
+ *   o     bf16 [T, H, d_latent] (the out argument of mla_decode); d_latent a multiple of 32
+ *   w_uv  bf16 [H, d_v, d_latent]: per head, each value column's d_latent weights contiguous
+ *         (w_uv[h, v, l] = W_UV[l, h, v] of the (L, N, V) weight); d_v a multiple of 64
+ *   out   bf16 [T, H, d_v]
+ * All pointers 16-byte aligned; fp32 accumulation, bf16 output rounded to nearest even. */
+int mla_v_up(int32_t tokens, int32_t num_heads, int32_t d_latent, int32_t d_v, const void* o,
+             const void* w_uv, void* out, void* stream);
 
 /* Static description of a status code. */
 const char* mla_strerror(int status);

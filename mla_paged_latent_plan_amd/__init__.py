@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import MLA_KV_BF16, MLA_KV_FP8, MLAError, Problem  # noqa: F401
 
 __all__ = ["Problem", "make_problem", "workspace_size", "mla_decode_plan", "mla_decode",
-           "mla_combine", "mla_kv_write", "MLADecode", "device_num_cus", "MLAError"]
+           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "MLADecode", "device_num_cus",
+           "MLAError"]
 
 
 def device_num_cus() -> int:
@@ -118,6 +119,40 @@ def mla_kv_write(p: Problem, kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mappin
     _lib.check("mla_kv_write", lib.mla_kv_write(
         p, n, _ptr(kv_c, torch.bfloat16, "kv_c"), _ptr(k_pe, torch.bfloat16, "k_pe"),
         _ptr(slot_mapping, torch.int64, "slot_mapping"), kv_cache.data_ptr(), _stream(stream)))
+
+
+def mla_q_absorb(q_nope: torch.Tensor, q_pe: Optional[torch.Tensor], w_uk: torch.Tensor,
+                 q_out: torch.Tensor, stream=None) -> None:
+    """q_out[t, h] = [q_nope[t, h] @ w_uk[h].T, q_pe[t, h]] (q_nope [T, H, P], w_uk [H, L, P])."""
+    lib = _lib.load()
+    T, H, P = q_nope.shape
+    L = int(w_uk.shape[1])
+    R = 0 if q_pe is None else int(q_pe.shape[2])
+    if tuple(w_uk.shape) != (H, L, P):
+        raise ValueError(f"w_uk must be [{H}, L, {P}], got {tuple(w_uk.shape)}")
+    if q_pe is not None and tuple(q_pe.shape) != (T, H, R):
+        raise ValueError(f"q_pe must be [{T}, {H}, R], got {tuple(q_pe.shape)}")
+    if q_out.numel() != T * H * (L + R) or q_out.shape[-1] != L + R:
+        raise ValueError(f"q_out must hold [{T}, {H}, {L + R}], got {tuple(q_out.shape)}")
+    _lib.check("mla_q_absorb", lib.mla_q_absorb(
+        T, H, P, L, R, _ptr(q_nope, torch.bfloat16, "q_nope"), _ptr(q_pe, torch.bfloat16, "q_pe"),
+        _ptr(w_uk, torch.bfloat16, "w_uk"), _ptr(q_out, torch.bfloat16, "q_out", T * H * (L + R)),
+        _stream(stream)))
+
+
+def mla_v_up(o: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """out[t, h] = o[t, h] @ w_uv[h].T (o [T, H, L], w_uv [H, V, L], out [T, H, V])."""
+    lib = _lib.load()
+    o3 = o.reshape(-1, o.shape[-2], o.shape[-1])
+    T, H, L = o3.shape
+    V = int(w_uv.shape[1])
+    if tuple(w_uv.shape) != (H, V, L):
+        raise ValueError(f"w_uv must be [{H}, V, {L}], got {tuple(w_uv.shape)}")
+    if out.numel() != T * H * V:
+        raise ValueError(f"out must hold [{T}, {H}, {V}], got {tuple(out.shape)}")
+    _lib.check("mla_v_up", lib.mla_v_up(
+        T, H, L, V, _ptr(o3, torch.bfloat16, "o"), _ptr(w_uv, torch.bfloat16, "w_uv"),
+        _ptr(out, torch.bfloat16, "out"), _stream(stream)))
 
 
 class MLADecode:

@@ -237,6 +237,61 @@ int mla_kv_write(const mla_problem* p, int64_t num_tokens, const void* kv_c, con
   return launch_rc(mla::launch_kv_write(a, sh.fmt, sh.d_qk - sh.d_rope,
                                         static_cast<hipStream_t>(stream)));
 }
+int mla_q_absorb(int32_t tokens, int32_t num_heads, int32_t d_nope, int32_t d_latent,
+                 int32_t d_rope, const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
+                 void* stream) {
+  if (tokens < 0 || num_heads < 1 || d_nope < 32 || d_nope % 32 != 0 || d_latent < 64 ||
+      d_latent % 64 != 0 || d_rope < 0 || d_rope % 8 != 0 || num_heads > 65535)
+    return MLA_ERR_SHAPE;
+  if (tokens == 0) return MLA_OK;
+  if (q_nope == nullptr || w_uk == nullptr || q_out == nullptr || (d_rope > 0 && q_pe == nullptr))
+    return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_out) ||
+      (d_rope > 0 && !aligned16(q_pe)))
+    return MLA_ERR_ALIGN;
+  mla::GemmArgs a;
+  a.a = static_cast<const uint16_t*>(q_nope);
+  a.a_t = (int64_t)num_heads * d_nope;
+  a.a_h = d_nope;
+  a.w = static_cast<const uint16_t*>(w_uk);
+  a.c = static_cast<uint16_t*>(q_out);
+  a.c_h = (int64_t)d_latent + d_rope;
+  a.c_t = (int64_t)num_heads * a.c_h;
+  a.pe = d_rope > 0 ? static_cast<const uint16_t*>(q_pe) : nullptr;
+  a.pe_t = (int64_t)num_heads * d_rope;
+  a.pe_h = d_rope;
+  a.T = tokens;
+  a.H = num_heads;
+  a.N = d_latent;
+  a.K = d_nope;
+  a.R = d_rope;
+  return launch_rc(mla::launch_absorb_gemm(a, static_cast<hipStream_t>(stream)));
+}
+int mla_v_up(int32_t tokens, int32_t num_heads, int32_t d_latent, int32_t d_v, const void* o,
+             const void* w_uv, void* out, void* stream) {
+  if (tokens < 0 || num_heads < 1 || d_latent < 32 || d_latent % 32 != 0 || d_v < 64 ||
+      d_v % 64 != 0 || num_heads > 65535)
+    return MLA_ERR_SHAPE;
+  if (tokens == 0) return MLA_OK;
+  if (o == nullptr || w_uv == nullptr || out == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(o) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  mla::GemmArgs a;
+  a.a = static_cast<const uint16_t*>(o);
+  a.a_t = (int64_t)num_heads * d_latent;
+  a.a_h = d_latent;
+  a.w = static_cast<const uint16_t*>(w_uv);
+  a.c = static_cast<uint16_t*>(out);
+  a.c_t = (int64_t)num_heads * d_v;
+  a.c_h = d_v;
+  a.pe = nullptr;
+  a.pe_t = a.pe_h = 0;
+  a.T = tokens;
+  a.H = num_heads;
+  a.N = d_v;
+  a.K = d_latent;
+  a.R = 0;
+  return launch_rc(mla::launch_absorb_gemm(a, static_cast<hipStream_t>(stream)));
+}
 const char* mla_strerror(int status) {
   switch (status) {
     case MLA_OK: return "ok";
