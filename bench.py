@@ -345,6 +345,11 @@ def bench_absorb(args):
     torch.cuda.synchronize()
     qa = np.array([a.elapsed_time(m) for a, m, _ in evs])
     vu = np.array([m.elapsed_time(e) for _, m, e in evs])
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     qa_bytes = 2 * (T * Hh * P + T * Hh * R + Hh * L * P + T * Hh * (L + R))
     vu_bytes = 2 * (T * Hh * L + Hh * V * L + T * Hh * V)
     flops = 2.0 * T * Hh * L * (P + V)
