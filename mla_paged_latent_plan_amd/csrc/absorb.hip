@@ -10,7 +10,8 @@
 // Both are C[t, n] = sum_k A[t, k] W[n, k] per head with k contiguous in A and W, so every MFMA
 // operand is one 16-byte load per lane (no transposition). The kernels compute C^T tiles,
 // D[n][t] = W[n, :] . A[t, :], on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; each lane ends
-// with four consecutive n of one t and stores them as 8 bytes (bf16, round to nearest even).
+// with four consecutive n of one t (bf16, round to nearest even): the tiled kernel stores them as
+// 8 bytes, the weight-stationary kernel pairs lanes to store 16.
 // DeepSeek-V3 shapes run the weight-stationary kernel below; other shapes the tiled one: a
 // workgroup of four waves owns 64 n x 64 t of one head, wave w rows n0 + 16 w .. + 15 and all 64 t
 // (four 16 x 16 accumulators), operands straight from global memory with the next k step's five
@@ -106,28 +107,22 @@ __global__ __launch_bounds__(256) void absorb_gemm_kernel(GemmArgs a) {
 // compute unit once per token chunk and each token row once per weight slice, instead of once per
 // 64 x 64 output tile. Used when the slice fits in LDS; NT accumulator tiles per wave.
 template <int K, int NT>
-__global__ __launch_bounds__(512) void absorb_ws_kernel(GemmArgs a, int t_chunk) {
+__global__ __launch_bounds__(512) void absorb_ws_kernel(GemmArgs a, int t_chunk, int chunks,
+                                                        int slices) {
   constexpr int kRow = 2 * K + 16;  // LDS bytes per weight row
   constexpr int NS = 16 * NT;       // weight rows (output columns) per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t lds[NS * kRow];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int h = blockIdx.z;
-  const int n0 = blockIdx.y * NS;
-  const int t_begin = blockIdx.x * t_chunk;
+  // Workgroups are dealt to the 8 XCDs round-robin: workgroup b runs on XCD b mod 8. All token
+  // chunks of a (head, slice) share that XCD, so its L2 fetches the weight slice from memory once.
+  const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int chunk = q % chunks, slice = (q / chunks) % slices;
+  const int h = (q / chunks / slices) * 8 + x;
+  if (h >= a.H) return;
+  const int n0 = slice * NS;
+  const int t_begin = chunk * t_chunk;
   const int t_end = min(a.T, t_begin + t_chunk);
-
-  // stage the weight slice: rows n0 .. n0 + NS - 1 of head h, 16 bytes per thread per pass
-  {
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.w + ((int64_t)h * a.N + n0) * K);
-    constexpr int kChunks = NS * (2 * K / 16);
-    for (int c = threadIdx.x; c < kChunks; c += blockDim.x) {
-      const int row = c / (2 * K / 16), col = c % (2 * K / 16);
-      *reinterpret_cast<u32x4*>(lds + row * kRow + 16 * col) =
-          *reinterpret_cast<const u32x4*>(src + (int64_t)row * 2 * K + 16 * col);
-    }
-  }
-  __syncthreads();
 
   const int r16 = lane & 15, kq = 8 * (lane >> 4);
   // token rows of a tile (the MFMA B operand for every k step); rows past T repeat row T - 1
@@ -139,7 +134,31 @@ __global__ __launch_bounds__(512) void absorb_ws_kernel(GemmArgs a, int t_chunk)
   };
   bf16x8 acur[K / 32], anxt[K / 32];
   int t0 = t_begin + 16 * wave;
-  if (t0 < t_end) load_tile(t0, acur);
+  if (t0 < t_end) load_tile(t0, acur);  // in flight during the staging below
+
+  // stage the weight slice (rows n0 .. n0 + NS - 1 of head h): each thread moves 16-byte pieces
+  // c = tid + 512 j, eight loads in flight before their LDS stores
+  {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.w + ((int64_t)h * a.N + n0) * K);
+    constexpr int kPieces = NS * (2 * K / 16);
+    static_assert(kPieces % (512 * 8) == 0, "staging batches of eight pieces per thread");
+#pragma unroll 1
+    for (int j0 = 0; j0 < kPieces / 512; j0 += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = threadIdx.x + 512 * (j0 + j);
+        v[j] = *reinterpret_cast<const u32x4*>(src + (int64_t)(c / (2 * K / 16)) * 2 * K + 16 * (c % (2 * K / 16)));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = threadIdx.x + 512 * (j0 + j);
+        *reinterpret_cast<u32x4*>(lds + (c / (2 * K / 16)) * kRow + 16 * (c % (2 * K / 16))) = v[j];
+      }
+    }
+  }
+  __syncthreads();
+
   for (; t0 < t_end; t0 += 16 * 8) {
     // the next tile's rows are in flight while this tile runs
     if (t0 + 16 * 8 < t_end) load_tile(t0 + 16 * 8, anxt);
@@ -156,14 +175,26 @@ __global__ __launch_bounds__(512) void absorb_ws_kernel(GemmArgs a, int t_chunk)
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the next step's LDS reads after these MFMAs
     }
-    // acc[i][e] = D[n0 + 16 i + 4 (lane >> 4) + e][t0 + r16]
-    if (t0 + r16 < a.T) {
-      uint16_t* cp = a.c + (int64_t)(t0 + r16) * a.c_t + (int64_t)h * a.c_h + n0 + 4 * (lane >> 4);
+    // acc[i][e] = D[n0 + 16 i + 4 g + e][t0 + r16], g = lane >> 4. Lanes g and g ^ 1 swap halves
+    // of a pair of tiles (i, i + 1) so that each holds eight consecutive columns: even g
+    // 16 i + 4 g .. + 7, odd g 16 (i + 1) + 4 (g - 1) .. + 7, one 16-byte store each.
+    {
+      const int g = lane >> 4;
+      const bool odd = g & 1;
+      uint16_t* cp = a.c + (int64_t)(t0 + r16) * a.c_t + (int64_t)h * a.c_h + n0;
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        const u32x2 v = {bf16_bits(acc[i][0]) | (bf16_bits(acc[i][1]) << 16),
-                         bf16_bits(acc[i][2]) | (bf16_bits(acc[i][3]) << 16)};
-        *reinterpret_cast<u32x2*>(cp + 16 * i) = v;
+      for (int i = 0; i < NT; i += 2) {
+        const u32x2 v0 = {bf16_bits(acc[i][0]) | (bf16_bits(acc[i][1]) << 16),
+                          bf16_bits(acc[i][2]) | (bf16_bits(acc[i][3]) << 16)};
+        const u32x2 v1 = {bf16_bits(acc[i + 1][0]) | (bf16_bits(acc[i + 1][1]) << 16),
+                          bf16_bits(acc[i + 1][2]) | (bf16_bits(acc[i + 1][3]) << 16)};
+        const u32x2 send = odd ? v0 : v1;
+        const u32x2 recv = {(uint32_t)__shfl_xor((int)send[0], 16, 64),
+                            (uint32_t)__shfl_xor((int)send[1], 16, 64)};
+        const u32x4 w = odd ? u32x4{recv[0], recv[1], v1[0], v1[1]}
+                            : u32x4{v0[0], v0[1], recv[0], recv[1]};
+        const int col = odd ? 16 * (i + 1) + 4 * (g - 1) : 16 * i + 4 * g;
+        if (t0 + r16 < a.T) *reinterpret_cast<u32x4*>(cp + col) = w;
       }
     }
 #pragma unroll
@@ -171,26 +202,33 @@ __global__ __launch_bounds__(512) void absorb_ws_kernel(GemmArgs a, int t_chunk)
   }
 
   // the query's RoPE tail, copied after the latent columns by the first slice's workgroups
-  if (a.pe != nullptr && blockIdx.y == 0) {
-    const int chunks = a.R / 8;
-    for (int idx = threadIdx.x; idx < (t_end - t_begin) * chunks; idx += blockDim.x) {
-      const int tt = t_begin + idx / chunks, c = idx % chunks;
+  if (a.pe != nullptr && slice == 0) {
+    const int pieces = a.R / 8;
+    for (int idx = threadIdx.x; idx < (t_end - t_begin) * pieces; idx += blockDim.x) {
+      const int tt = t_begin + idx / pieces, c = idx % pieces;
       const u32x4 v = *reinterpret_cast<const u32x4*>(a.pe + (int64_t)tt * a.pe_t + (int64_t)h * a.pe_h + 8 * c);
       *reinterpret_cast<u32x4*>(a.c + (int64_t)tt * a.c_t + (int64_t)h * a.c_h + a.N + 8 * c) = v;
     }
   }
 }
 
-// Weight-stationary launch for (K, slice rows): the slice count is the smallest that gives every
-// compute unit a workgroup, token chunks of 256 (fewer when that leaves compute units idle).
+// Weight-stationary launch for (K, slice rows): token chunks as long as possible (each chunk
+// re-reads the weight slice) while the grid still fills every compute unit; chunks are whole
+// 16-token tiles.
 template <int K, int NT>
 hipError_t launch_ws(const GemmArgs& a, hipStream_t s) {
   constexpr int NS = 16 * NT;
+  static_assert(NT % 2 == 0, "output columns are stored in pairs of 16-column tiles");
+  // workgroups one compute unit can hold (LDS): two for the 70 KB query-absorption slice
+  constexpr int kPerCu = (NS * (2 * K + 16) <= 80 * 1024) ? 2 : 1;
   const int slices = a.N / NS;
-  int t_chunk = 256;
-  while (t_chunk > 16 && (int64_t)((a.T + t_chunk - 1) / t_chunk) * slices * a.H < 256) t_chunk /= 2;
-  const dim3 grid((unsigned)((a.T + t_chunk - 1) / t_chunk), (unsigned)slices, (unsigned)a.H);
-  hipLaunchKernelGGL((absorb_ws_kernel<K, NT>), grid, dim3(512), 0, s, a, t_chunk);
+  int t_chunk = (a.T + 15) / 16 * 16;
+  while (t_chunk > 16 && (int64_t)((a.T + t_chunk - 1) / t_chunk) * slices * a.H < 256 * kPerCu)
+    t_chunk = (t_chunk / 2 + 15) / 16 * 16;
+  const int chunks = (a.T + t_chunk - 1) / t_chunk;
+  const int64_t grid = (int64_t)chunks * slices * ((a.H + 7) / 8) * 8;
+  hipLaunchKernelGGL((absorb_ws_kernel<K, NT>), dim3((unsigned)grid), dim3(512), 0, s, a, t_chunk,
+                     chunks, slices);
   return hipGetLastError();
 }
 
