@@ -140,3 +140,24 @@ def test_kv_write_host_checks(lib):
     bad = good(page_size=24)
     assert lib.mla_kv_write(ctypes.byref(bad), i64(4), vp(4096), vp(4096), vp(4096), vp(4096),
                             None) == 4
+
+
+def test_absorb_host_checks(lib):
+    vp = ctypes.c_void_p
+    # no tokens: nothing to check or enqueue
+    assert lib.mla_q_absorb(0, 128, 128, 512, 64, None, None, None, None, None) == 0
+    assert lib.mla_v_up(0, 128, 512, 128, None, None, None, None) == 0
+    # shapes: negative tokens, k not a multiple of 32, columns not a multiple of 64, odd RoPE width
+    assert lib.mla_q_absorb(-1, 128, 128, 512, 64, vp(4096), vp(4096), vp(4096), vp(4096), None) == 2
+    assert lib.mla_q_absorb(4, 128, 100, 512, 64, vp(4096), vp(4096), vp(4096), vp(4096), None) == 2
+    assert lib.mla_q_absorb(4, 128, 128, 500, 64, vp(4096), vp(4096), vp(4096), vp(4096), None) == 2
+    assert lib.mla_q_absorb(4, 128, 128, 512, 60, vp(4096), vp(4096), vp(4096), vp(4096), None) == 2
+    assert lib.mla_v_up(4, 128, 500, 128, vp(4096), vp(4096), vp(4096), None) == 2
+    assert lib.mla_v_up(4, 128, 512, 100, vp(4096), vp(4096), vp(4096), None) == 2
+    # null operands; q_pe may be NULL only without a RoPE part
+    assert lib.mla_q_absorb(4, 128, 128, 512, 64, vp(4096), None, vp(4096), vp(4096), None) == 1
+    assert lib.mla_q_absorb(4, 128, 128, 512, 64, vp(4096), vp(4096), None, vp(4096), None) == 1
+    assert lib.mla_v_up(4, 128, 512, 128, None, vp(4096), vp(4096), None) == 1
+    # alignment
+    assert lib.mla_q_absorb(4, 128, 128, 512, 64, vp(4104), vp(4096), vp(4096), vp(4096), None) == 7
+    assert lib.mla_v_up(4, 128, 512, 128, vp(4096), vp(4096), vp(4100), None) == 7
