@@ -15,6 +15,7 @@ Everything is computed in float64 with numpy on dense, unpaged rows:
 - plan.py      the split/work-unit plan, integer arithmetic
 - kvwrite.py   writing new tokens' rows into the paged cache (bf16 copy, fp8 quantisation)
 - absorb.py    per-head weight absorption before (W_UK) and up-projection after (W_UV) the decode
+- swa_runs.py  sliding windows of cache slots compressed into at most two runs per token
 
 Parity status of each function is stated in its module docstring.
 """
