@@ -23,6 +23,10 @@
  *   mla_q_absorb     the decode's query [q_nope x W_UK, q_pe] from the per-head query parts
  *   mla_v_up         the per-head output o x W_UV from the decode's latent output
  *
+ * and, for caches whose sliding windows are given as lists of slots, their run-compressed form:
+ *
+ *   mla_swa_runs     each token's window of slots as at most two runs of consecutive slots
+ *
  * Conventions shared by every call
  * - All pointers are device pointers unless a parameter says "host". The caller owns every buffer;
  *   the library never allocates, frees or synchronises. `stream` is a hipStream_t (NULL = default
@@ -176,6 +180,24 @@ int mla_q_absorb(int32_t tokens, int32_t num_heads, int32_t d_nope, int32_t d_la
  * All pointers 16-byte aligned; fp32 accumulation, bf16 output rounded to nearest even. */
 int mla_v_up(int32_t tokens, int32_t num_heads, int32_t d_latent, int32_t d_v, const void* o,
              const void* w_uv, void* out, void* stream);
+
+/* Run-compressed sliding windows (HALOps MLA API, mla_attention_plan: each token's SWA window is
+ * compressed into at most two runs of consecutive slots; a run ends where the next slot is not the
+ * previous one plus kv_run_step or lies on another page; a window of more than two runs, a padding
+ * or not yet written window, is cut to its first row).
+ *   tokens        T >= 0 (0 enqueues nothing); topk >= 1 columns per window
+ *   kv_indices    int32 [T, topk]: the cache slots of each token's window rows, in row order;
+ *                 columns past the token's length are ignored
+ *   topk_lengths  int32 [T] rows per window (clamped to [0, topk]), or NULL for topk rows
+ *   page_size     rows per cache page, a power of two; page of a slot = floor(slot / page_size)
+ *   kv_run_step   1 or -1: the slot step between consecutive rows of a run
+ *   runs          int32 [T, 4], 16-byte aligned (out): (slot0, len0, slot1, rows); rows g < len0 at
+ *                 slot0 + kv_run_step * g, the others at slot1 + kv_run_step * (g - len0); slot1 = -1
+ *                 when len0 = rows; an empty window gives (-1, 0, -1, 0) and a cut one
+ *                 (slot of row 0, 1, -1, 1). */
+int mla_swa_runs(int32_t tokens, int32_t topk, const int32_t* kv_indices,
+                 const int32_t* topk_lengths, int32_t page_size, int32_t kv_run_step, int32_t* runs,
+                 void* stream);
 
 /* Static description of a status code. */
 const char* mla_strerror(int status);

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import MLA_KV_BF16, MLA_KV_FP8, MLAError, Problem  # noqa: F401
 
 __all__ = ["Problem", "make_problem", "workspace_size", "mla_decode_plan", "mla_decode",
-           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "MLADecode", "device_num_cus",
+           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "MLADecode", "device_num_cus",
            "MLAError"]
 
 
@@ -153,6 +153,19 @@ def mla_v_up(o: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor, stream=None
     _lib.check("mla_v_up", lib.mla_v_up(
         T, H, L, V, _ptr(o3, torch.bfloat16, "o"), _ptr(w_uv, torch.bfloat16, "w_uv"),
         _ptr(out, torch.bfloat16, "out"), _stream(stream)))
+
+
+def mla_swa_runs(kv_indices: torch.Tensor, topk_lengths: Optional[torch.Tensor], page_size: int,
+                 kv_run_step: int, runs: torch.Tensor, stream=None) -> None:
+    """runs[t] = (slot0, len0, slot1, rows): token t's window of slots as at most two runs."""
+    lib = _lib.load()
+    T, topk = kv_indices.shape
+    if tuple(runs.shape) != (T, 4):
+        raise ValueError(f"runs must be [{T}, 4], got {tuple(runs.shape)}")
+    _lib.check("mla_swa_runs", lib.mla_swa_runs(
+        T, topk, _ptr(kv_indices, torch.int32, "kv_indices"),
+        _ptr(topk_lengths, torch.int32, "topk_lengths", T), int(page_size), int(kv_run_step),
+        _ptr(runs, torch.int32, "runs"), _stream(stream)))
 
 
 class MLADecode:

@@ -292,6 +292,29 @@ int mla_v_up(int32_t tokens, int32_t num_heads, int32_t d_latent, int32_t d_v, c
   a.R = 0;
   return launch_rc(mla::launch_absorb_gemm(a, static_cast<hipStream_t>(stream)));
 }
+int mla_swa_runs(int32_t tokens, int32_t topk, const int32_t* kv_indices,
+                 const int32_t* topk_lengths, int32_t page_size, int32_t kv_run_step, int32_t* runs,
+                 void* stream) {
+  if (tokens < 0 || topk < 1) return MLA_ERR_SHAPE;
+  if (!is_pow2(page_size) || page_size > (1 << 30)) return MLA_ERR_PAGE;
+  if (kv_run_step != 1 && kv_run_step != -1) return MLA_ERR_MODE;
+  if (tokens == 0) return MLA_OK;
+  if (kv_indices == nullptr || runs == nullptr) return MLA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(kv_indices) & 3u) != 0 || !aligned16(runs) ||
+      (topk_lengths != nullptr && (reinterpret_cast<uintptr_t>(topk_lengths) & 3u) != 0))
+    return MLA_ERR_ALIGN;
+  mla::SwaRunsArgs a;
+  a.kv = kv_indices;
+  a.lengths = topk_lengths;
+  a.runs = runs;
+  a.T = tokens;
+  a.topk = topk;
+  int lg = 0;
+  while ((1 << lg) < page_size) ++lg;
+  a.ps_log2 = lg;
+  a.step = kv_run_step;
+  return launch_rc(mla::launch_swa_runs(a, static_cast<hipStream_t>(stream)));
+}
 const char* mla_strerror(int status) {
   switch (status) {
     case MLA_OK: return "ok";

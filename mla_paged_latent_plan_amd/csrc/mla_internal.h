@@ -116,11 +116,20 @@ struct GemmArgs {
   int T, H, N, K, R;
 };
 
+struct SwaRunsArgs {
+  const int32_t* kv;       // [T][topk] window slots
+  const int32_t* lengths;  // [T] or nullptr
+  int32_t* runs;           // [T][4]
+  int64_t T;
+  int topk, ps_log2, step;
+};
+
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, const Shape& sh, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_kv_write(const KvWriteArgs& a, int fmt, int d_nope, hipStream_t s);
 hipError_t launch_absorb_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_swa_runs(const SwaRunsArgs& a, hipStream_t s);
 
 }  // namespace mla

@@ -161,3 +161,15 @@ def test_absorb_host_checks(lib):
     # alignment
     assert lib.mla_q_absorb(4, 128, 128, 512, 64, vp(4104), vp(4096), vp(4096), vp(4096), None) == 7
     assert lib.mla_v_up(4, 128, 512, 128, vp(4096), vp(4096), vp(4100), None) == 7
+
+
+def test_swa_runs_host_checks(lib):
+    vp = ctypes.c_void_p
+    assert lib.mla_swa_runs(0, 128, None, None, 64, 1, None, None) == 0
+    assert lib.mla_swa_runs(-1, 128, vp(4096), None, 64, 1, vp(4096), None) == 2
+    assert lib.mla_swa_runs(4, 0, vp(4096), None, 64, 1, vp(4096), None) == 2
+    assert lib.mla_swa_runs(4, 128, vp(4096), None, 48, 1, vp(4096), None) == 4
+    assert lib.mla_swa_runs(4, 128, vp(4096), None, 64, 2, vp(4096), None) == 5
+    assert lib.mla_swa_runs(4, 128, None, None, 64, 1, vp(4096), None) == 1
+    assert lib.mla_swa_runs(4, 128, vp(4096), None, 64, 1, vp(4104), None) == 7
+    assert lib.mla_swa_runs(4, 128, vp(4098), None, 64, 1, vp(4096), None) == 7
