@@ -40,12 +40,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=None,
                     help="workload: 2 (default for decode), 1, 3 (default for kv_write), 4, 5, s1, s4")
-    ap.add_argument("--op", choices=("decode", "kv_write", "absorb"), default="decode",
+    ap.add_argument("--op", choices=("decode", "kv_write", "absorb", "swa_runs"), default="decode",
                     help="decode: mla_decode + mla_combine (the default); kv_write: mla_kv_write "
                          "of every row of the workload's requests in one launch; absorb: "
                          "mla_q_absorb + mla_v_up for --tokens query tokens (DeepSeek-V3 dims)")
     ap.add_argument("--tokens", type=int, default=64,
-                    help="absorb: query tokens (64 = the dsv3 decode batch)")
+                    help="absorb: query tokens (64 = the dsv3 decode batch); swa_runs: tokens "
+                         "(default 640)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -401,6 +402,59 @@ def bench_absorb(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_swa_runs(args):
+    """mla_swa_runs over T tokens' 128-row windows (+ 3 drafts) in a ring of slots, pages of 64:
+    the plan step of sliding-window layers, run once per forward."""
+    import torch
+    import mla_paged_latent_plan_amd as mla
+    T = args.tokens if args.tokens != 64 else 640
+    topk, page = 131, 64
+    g = np.random.default_rng(3000 + T)
+    base = g.integers(0, 1 << 20, T)
+    kv = (base[:, None] + np.arange(topk)[None, :]).astype(np.int32)  # mostly one or two runs
+    lengths = g.integers(1, topk + 1, T).astype(np.int32)
+    dev = torch.device("cuda:0")
+    kv_d, len_d = torch.from_numpy(kv).to(dev), torch.from_numpy(lengths).to(dev)
+    runs = torch.empty(T, 4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        mla.mla_swa_runs(kv_d, len_d, page, 1, runs, stream)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(ev(), ev()) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        mla.mla_swa_runs(kv_d, len_d, page, 1, runs, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    nbytes = T * topk * 4 + T * 4 + T * 16
+    t = float(ms.mean()) / 1e3
+    res = {
+        "metric": "MLA sliding-window run plan: tokens/s, achieved HBM GB/s",
+        "value": round(T / t, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": f"swa_runs: {T} tokens x {topk}-slot windows, pages of {page}",
+                   "tokens": T, "parallelism": "single-gpu"},
+        "roofline": dict(bound="hbm", achieved=round(nbytes / t / 1e9, 1), peak=HBM_PEAK_GBS,
+                         unit="GB/s", frac=round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), traffic=None),
+        "note": "latency-bound: one launch over a few hundred KB",
+    }
+    if not args.no_cpu:
+        from oracle import swa_runs
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            swa_runs.swa_runs(kv, lengths, page, 1)
+            n += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = dict(value=round(n * T / dt, 1), unit="tokens/s", cores=1,
+                                   kind="oracle", sample=f"{n} pass(es) over all {T} tokens, "
+                                                         f"pure-Python oracle, {dt:.1f} s")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -411,6 +465,8 @@ def main():
         return bench_kv_write(args)
     if args.op == "absorb":
         return bench_absorb(args)
+    if args.op == "swa_runs":
+        return bench_swa_runs(args)
     import torch
     import mla_paged_latent_plan_amd as mla
     from workloads import make

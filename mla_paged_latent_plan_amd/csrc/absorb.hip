@@ -16,7 +16,7 @@
 // workgroup of four waves owns 64 n x 64 t of one head, wave w rows n0 + 16 w .. + 15 and all 64 t
 // (four 16 x 16 accumulators), operands straight from global memory with the next k step's five
 // loads issued before the current step's four MFMAs.
-#include "mla_internal.h"
+#include "layer_internal.h"
 
 namespace mla {
 

@@ -2,6 +2,7 @@
 // and kernel dispatch. Every check runs on the host before anything is enqueued.
 #include "../../include/mla.h"
 #include "mla_internal.h"
+#include "layer_internal.h"
 
 #include <math.h>
 

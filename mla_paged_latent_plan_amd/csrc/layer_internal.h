@@ -1,0 +1,33 @@
+// Internal definitions of the kernels around the decode (absorption GEMMs, sliding-window run
+// plan) shared with the C-ABI layer.
+#pragma once
+
+#include "mla_internal.h"
+
+namespace mla {
+
+// Per-head NT GEMM C[t, h, n] = sum_k A[t, h, k] W[h, n, k] (bf16 in/out, fp32 accumulation),
+// optionally followed by a copy of pe[t, h, 0:R] into C[t, h, N:N+R]. Strides in elements.
+struct GemmArgs {
+  const uint16_t* a;
+  int64_t a_t, a_h;
+  const uint16_t* w;  // [H][N][K]
+  uint16_t* c;
+  int64_t c_t, c_h;
+  const uint16_t* pe;  // nullable
+  int64_t pe_t, pe_h;
+  int T, H, N, K, R;
+};
+
+struct SwaRunsArgs {
+  const int32_t* kv;       // [T][topk] window slots
+  const int32_t* lengths;  // [T] or nullptr
+  int32_t* runs;           // [T][4]
+  int64_t T;
+  int topk, ps_log2, step;
+};
+
+hipError_t launch_absorb_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_swa_runs(const SwaRunsArgs& a, hipStream_t s);
+
+}  // namespace mla

@@ -103,33 +103,10 @@ struct KvWriteArgs {
   int ps_log2;
 };
 
-// Per-head NT GEMM C[t, h, n] = sum_k A[t, h, k] W[h, n, k] (bf16 in/out, fp32 accumulation),
-// optionally followed by a copy of pe[t, h, 0:R] into C[t, h, N:N+R]. Strides in elements.
-struct GemmArgs {
-  const uint16_t* a;
-  int64_t a_t, a_h;
-  const uint16_t* w;  // [H][N][K]
-  uint16_t* c;
-  int64_t c_t, c_h;
-  const uint16_t* pe;  // nullable
-  int64_t pe_t, pe_h;
-  int T, H, N, K, R;
-};
-
-struct SwaRunsArgs {
-  const int32_t* kv;       // [T][topk] window slots
-  const int32_t* lengths;  // [T] or nullptr
-  int32_t* runs;           // [T][4]
-  int64_t T;
-  int topk, ps_log2, step;
-};
-
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, const Shape& sh, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_kv_write(const KvWriteArgs& a, int fmt, int d_nope, hipStream_t s);
-hipError_t launch_absorb_gemm(const GemmArgs& a, hipStream_t s);
-hipError_t launch_swa_runs(const SwaRunsArgs& a, hipStream_t s);
 
 }  // namespace mla

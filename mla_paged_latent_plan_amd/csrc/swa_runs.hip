@@ -9,7 +9,7 @@
 // does not continue the previous one, or a page change, page = slot >> log2(page_size), i.e. floor
 // division also for negative padding slots); a ballot gives the chunk's starts, the first start is
 // the lowest set bit, and the wave stops once two starts are seen.
-#include "mla_internal.h"
+#include "layer_internal.h"
 
 namespace mla {
 
