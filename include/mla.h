@@ -27,6 +27,10 @@
  *
  *   mla_swa_runs     each token's window of slots as at most two runs of consecutive slots
  *
+ * and, for the chunked-context prefill, the gather of context rows into a bf16 workspace:
+ *
+ *   mla_gather_context  rows of the requests of one context chunk, widened to bf16
+ *
  * Conventions shared by every call
  * - All pointers are device pointers unless a parameter says "host". The caller owns every buffer;
  *   the library never allocates, frees or synchronises. `stream` is a hipStream_t (NULL = default
@@ -198,6 +202,26 @@ int mla_v_up(int32_t tokens, int32_t num_heads, int32_t d_latent, int32_t d_v, c
 int mla_swa_runs(int32_t tokens, int32_t topk, const int32_t* kv_indices,
                  const int32_t* topk_lengths, int32_t page_size, int32_t kv_run_step, int32_t* runs,
                  void* stream);
+
+/* Context gather (vLLM mla_attention.py _compute_prefill_context: gather_and_maybe_dequant_cache
+ * with cu_seq_lens, token_to_seq and seq_starts): output row i is row
+ * j = seq_starts[r] + i - cu_seq_lens[r] of request r = token_to_seq[i], read through block_table
+ * row r, as bf16. fp8 rows are widened exactly (e4m3 value times its group's ue8m0 scale; RoPE tail
+ * as stored); bf16 rows are copied.
+ *   p             the cache's problem (dims, format, page fields, max_pages_per_seq are used)
+ *   num_reqs      requests of the chunk (rows of block_table, entries of seq_starts)
+ *   num_rows      output rows n >= 0 (0 enqueues nothing)
+ *   block_table   int32 [num_reqs, max_pages_per_seq]
+ *   cu_seq_lens   int32 [num_reqs + 1]: output rows of request r are [cu_seq_lens[r], cu_seq_lens[r+1])
+ *   seq_starts    int32 [num_reqs]: first logical row of each request's span, or NULL for 0
+ *   token_to_seq  int32 [n]: request of each output row
+ *   dst           bf16 [n, d_qk], 16-byte aligned
+ * Rows whose position or page falls outside the block table or the cache are written as zeros.
+ * Indices into cu_seq_lens / seq_starts / block_table must be valid (token_to_seq < num_reqs). */
+int mla_gather_context(const mla_problem* p, int32_t num_reqs, int64_t num_rows,
+                       const int32_t* block_table, const int32_t* cu_seq_lens,
+                       const int32_t* seq_starts, const int32_t* token_to_seq, const void* kv_cache,
+                       void* dst, void* stream);
 
 /* Static description of a status code. */
 const char* mla_strerror(int status);

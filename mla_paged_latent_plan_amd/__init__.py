@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import MLA_KV_BF16, MLA_KV_FP8, MLAError, Problem  # noqa: F401
 
 __all__ = ["Problem", "make_problem", "workspace_size", "mla_decode_plan", "mla_decode",
-           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "MLADecode", "device_num_cus",
+           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "MLADecode", "device_num_cus",
            "MLAError"]
 
 
@@ -166,6 +166,28 @@ def mla_swa_runs(kv_indices: torch.Tensor, topk_lengths: Optional[torch.Tensor],
         T, topk, _ptr(kv_indices, torch.int32, "kv_indices"),
         _ptr(topk_lengths, torch.int32, "topk_lengths", T), int(page_size), int(kv_run_step),
         _ptr(runs, torch.int32, "runs"), _stream(stream)))
+
+
+def mla_gather_context(p: Problem, block_table: torch.Tensor, cu_seq_lens: torch.Tensor,
+                       seq_starts: Optional[torch.Tensor], token_to_seq: torch.Tensor,
+                       kv_cache: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """dst[i] = row seq_starts[r] + i - cu_seq_lens[r] of request r = token_to_seq[i], as bf16."""
+    lib = _lib.load()
+    n = int(token_to_seq.numel())
+    R = int(block_table.shape[0])
+    if tuple(block_table.shape) != (R, p.max_pages_per_seq):
+        raise ValueError("block_table must be [num_reqs, max_pages_per_seq]")
+    if cu_seq_lens.numel() != R + 1 or (seq_starts is not None and seq_starts.numel() != R):
+        raise ValueError("cu_seq_lens must hold num_reqs + 1 entries, seq_starts num_reqs")
+    if dst.numel() < n * p.d_qk:
+        raise ValueError(f"dst must hold [{n}, {p.d_qk}]")
+    if kv_cache.numel() * kv_cache.element_size() < p.num_pages * p.page_stride_bytes:
+        raise ValueError("kv_cache is smaller than num_pages * page_stride_bytes")
+    _lib.check("mla_gather_context", lib.mla_gather_context(
+        p, R, n, _ptr(block_table, torch.int32, "block_table"),
+        _ptr(cu_seq_lens, torch.int32, "cu_seq_lens"), _ptr(seq_starts, torch.int32, "seq_starts"),
+        _ptr(token_to_seq, torch.int32, "token_to_seq"), kv_cache.data_ptr(),
+        _ptr(dst, torch.bfloat16, "dst"), _stream(stream)))
 
 
 class MLADecode:

@@ -316,6 +316,34 @@ int mla_swa_runs(int32_t tokens, int32_t topk, const int32_t* kv_indices,
   a.step = kv_run_step;
   return launch_rc(mla::launch_swa_runs(a, static_cast<hipStream_t>(stream)));
 }
+int mla_gather_context(const mla_problem* p, int32_t num_reqs, int64_t num_rows,
+                       const int32_t* block_table, const int32_t* cu_seq_lens,
+                       const int32_t* seq_starts, const int32_t* token_to_seq, const void* kv_cache,
+                       void* dst, void* stream) {
+  Shape sh;
+  int rc = derive(p, 1, &sh);
+  if (rc != MLA_OK) return rc;
+  if (num_reqs < 1 || num_rows < 0 || num_rows > (int64_t)INT32_MAX * 4) return MLA_ERR_SHAPE;
+  if (num_rows == 0) return MLA_OK;
+  if (block_table == nullptr || cu_seq_lens == nullptr || token_to_seq == nullptr ||
+      kv_cache == nullptr || dst == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned16(kv_cache) || !aligned16(dst)) return MLA_ERR_ALIGN;
+  mla::GatherArgs a;
+  a.cache = static_cast<const uint8_t*>(kv_cache);
+  a.block_table = block_table;
+  a.cu_seq_lens = cu_seq_lens;
+  a.seq_starts = seq_starts;
+  a.token_to_seq = token_to_seq;
+  a.dst = static_cast<uint16_t*>(dst);
+  a.n = num_rows;
+  a.page_stride = sh.page_stride;
+  a.num_pages = sh.num_pages;
+  a.scale_off = (int64_t)sh.page_size * sh.row_bytes;
+  a.max_pages = sh.max_pages;
+  a.ps_log2 = sh.ps_log2;
+  return launch_rc(mla::launch_gather(a, sh.fmt, sh.d_qk, static_cast<hipStream_t>(stream)));
+}
 const char* mla_strerror(int status) {
   switch (status) {
     case MLA_OK: return "ok";

@@ -1,5 +1,5 @@
 // Internal definitions of the kernels around the decode (absorption GEMMs, sliding-window run
-// plan) shared with the C-ABI layer.
+// plan, context gather) shared with the C-ABI layer.
 #pragma once
 
 #include "mla_internal.h"
@@ -27,7 +27,19 @@ struct SwaRunsArgs {
   int topk, ps_log2, step;
 };
 
+struct GatherArgs {
+  const uint8_t* cache;
+  const int32_t* block_table;   // [num_reqs][max_pages]
+  const int32_t* cu_seq_lens;   // [num_reqs + 1]
+  const int32_t* seq_starts;    // [num_reqs] or nullptr
+  const int32_t* token_to_seq;  // [n]
+  uint16_t* dst;                // bf16 [n][d_qk]
+  int64_t n, page_stride, num_pages, scale_off;
+  int max_pages, ps_log2;
+};
+
 hipError_t launch_absorb_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, int fmt, int d_qk, hipStream_t s);
 hipError_t launch_swa_runs(const SwaRunsArgs& a, hipStream_t s);
 
 }  // namespace mla

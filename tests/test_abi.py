@@ -173,3 +173,17 @@ def test_swa_runs_host_checks(lib):
     assert lib.mla_swa_runs(4, 128, None, None, 64, 1, vp(4096), None) == 1
     assert lib.mla_swa_runs(4, 128, vp(4096), None, 64, 1, vp(4104), None) == 7
     assert lib.mla_swa_runs(4, 128, vp(4098), None, 64, 1, vp(4096), None) == 7
+
+
+def test_gather_host_checks(lib):
+    p = good()
+    vp = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    assert lib.mla_gather_context(ctypes.byref(p), 1, i64(0), None, None, None, None, None, None,
+                                  None) == 0
+    assert lib.mla_gather_context(ctypes.byref(p), 0, i64(4), vp(4096), vp(4096), None, vp(4096),
+                                  vp(4096), vp(4096), None) == 2
+    assert lib.mla_gather_context(ctypes.byref(p), 1, i64(4), None, vp(4096), None, vp(4096),
+                                  vp(4096), vp(4096), None) == 1
+    assert lib.mla_gather_context(ctypes.byref(p), 1, i64(4), vp(4096), vp(4096), None, vp(4096),
+                                  vp(4096), vp(4100), None) == 7
