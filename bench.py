@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=None,
                     help="workload: 2 (default for decode), 1, 3 (default for kv_write), 4, 5, s1, s4")
-    ap.add_argument("--op", choices=("decode", "kv_write", "absorb", "swa_runs"), default="decode",
+    ap.add_argument("--op", choices=("decode", "kv_write", "absorb", "swa_runs", "gather"), default="decode",
                     help="decode: mla_decode + mla_combine (the default); kv_write: mla_kv_write "
                          "of every row of the workload's requests in one launch; absorb: "
                          "mla_q_absorb + mla_v_up for --tokens query tokens (DeepSeek-V3 dims)")
@@ -455,6 +455,80 @@ def bench_swa_runs(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_gather(args):
+    """mla_gather_context of the whole context of every request of the workload in one launch (the
+    rows a chunked-context prefill over these contexts gathers), fp8 rows widened to bf16."""
+    import torch
+    import mla_paged_latent_plan_amd as mla
+    from workloads import make
+    from workloads.gen import cache_layout
+
+    s = get_spec(args.config or "3")
+    wl = make(s)
+    dev = torch.device("cuda:0")
+    lay = cache_layout(s.kv_format, s.d_qk, s.d_rope, s.page_size)
+    lens = np.maximum(wl.seqlens.astype(np.int64), 0)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    t2s = np.repeat(np.arange(s.batch), lens).astype(np.int32)
+    n = int(cu[-1])
+    p = mla.make_problem(s.batch, s.q_len, s.num_heads, s.d_qk,
+                         mla.MLA_KV_BF16 if s.kv_format == "bf16" else mla.MLA_KV_FP8,
+                         s.page_size, wl.page_stride, wl.num_pages, int(wl.block_table.shape[1]))
+    bt, cu_d, t2s_d = wl.block_table.to(dev), torch.from_numpy(cu).to(dev), torch.from_numpy(t2s).to(dev)
+    cache = wl.cache.to(dev)
+    dst = torch.empty(n, s.d_qk, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sweep_out = torch.empty(1, dtype=torch.float32, device=dev)
+    run = lambda: mla.mla_gather_context(p, bt, cu_d, None, t2s_d, cache, dst, stream)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(ev(), ev()) for _ in range(args.steps)]
+    for a, b in evs:
+        if not args.no_flush:
+            torch.sum(sweep, dim=0, out=sweep_out[0])
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    in_row = lay["row_bytes"] + (8 if s.kv_format == "fp8" else 0)
+    nbytes = n * (in_row + 2 * s.d_qk + 4) + 4 * (s.batch + 1) + 4 * int(np.sum(-(-lens // s.page_size)))
+    t = float(ms.mean()) / 1e3
+    gbs = nbytes / t / 1e9
+    res = {
+        "metric": "MLA context gather: rows/s, achieved HBM GB/s, % of roofline",
+        "value": round(n / t, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": ("fp8-e4m3/ue8m0" if s.kv_format == "fp8" else "bf16") + "->bf16",
+        "data": "synthetic",
+        "config": {"workload": f"gather {s.name}: all {n} context rows of {s.batch} requests, "
+                               f"pages of {s.page_size}", "rows": n, "parallelism": "single-gpu"},
+        "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None),
+        "ms_p10_p90": [round(float(np.percentile(ms, 10)), 4), round(float(np.percentile(ms, 90)), 4)],
+        "algorithmic_bytes": int(nbytes),
+        "cache_eviction": "none" if args.no_flush else "read-only 1 GiB sweep",
+    }
+    if not args.no_cpu:
+        from oracle import gather
+        cache_h, bt_h = wl.cache.numpy(), wl.block_table.numpy()
+        k, passes = min(n, 4000), 0
+        t0 = time.perf_counter()
+        while passes == 0 or time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            gather.gather_context(cache_h, bt_h, cu, None, t2s[:k], s.kv_format, s.d_qk, s.d_rope,
+                                  s.page_size)  # output rows 0 .. k - 1 of the same gather
+            passes += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = dict(value=round(passes * k / dt, 1), unit="rows/s", cores=1,
+                                   kind="oracle", sample=f"{passes} pass(es) over the first {k} "
+                                   f"output rows, float64 numpy oracle (oracle/gather.py), {dt:.1f} s")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -467,6 +541,8 @@ def main():
         return bench_absorb(args)
     if args.op == "swa_runs":
         return bench_swa_runs(args)
+    if args.op == "gather":
+        return bench_gather(args)
     import torch
     import mla_paged_latent_plan_amd as mla
     from workloads import make
