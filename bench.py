@@ -494,6 +494,11 @@ def bench_gather(args):
         b.record(stream)
     torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(b) for a, b in evs])
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     in_row = lay["row_bytes"] + (8 if s.kv_format == "fp8" else 0)
     nbytes = n * (in_row + 2 * s.d_qk + 4) + 4 * (s.batch + 1) + 4 * int(np.sum(-(-lens // s.page_size)))
     t = float(ms.mean()) / 1e3
