@@ -209,3 +209,30 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16)), f"replay {k}: out"
         assert torch.equal(lse, l_ref), f"replay {k}: lse"
+
+
+@pytest.mark.parametrize("case", ["max_groups", "max_page", "h32_tiles"])
+def test_maximum_sizes(case):
+    """Limits of the library: the plan's 8192 query groups (per-group state held in LDS), pages of
+    4096 rows (the largest accepted), and the 32-row tile (17..32 stacked rows) that no benchmark
+    workload uses."""
+    if case == "max_groups":
+        rng = np.random.default_rng(71)
+        lens = rng.integers(0, 40, 8192).astype(np.int32)  # empty requests included
+        spec = Spec("max_groups", batch=8192, q_len=1, num_heads=16, page_size=16,
+                    seqlens=tuple(int(x) for x in lens), sm_scale=S, seed=71)
+    elif case == "max_page":
+        spec = Spec("max_page", batch=2, q_len=1, num_heads=128, page_size=4096,
+                    seqlens=(5000, 4096), sm_scale=S, seed=72)
+    else:
+        spec = Spec("h32_tiles", batch=5, q_len=2, num_heads=16, page_size=64,
+                    seqlens=(2, 65, 700, 1999, 64), causal=True, sm_scale=S, seed=73)
+    wl = make(spec)
+    print(f"[gpu] maximum sizes: {case}", flush=True)
+    out, lse, plan, used = H.run_gpu(wl)
+    O, L, A = H.oracle_of(wl, abs_mass=True)
+    m = H.metrics(out, lse, O, L, A)
+    print(f"[gpu]   {m}", flush=True)
+    H.assert_parity(m, ctx=case)
+    want = H.plan_words(wl, used)
+    assert np.array_equal(plan.view(torch.int32).numpy()[:len(want)], want)
