@@ -137,25 +137,9 @@ __device__ __forceinline__ bf16x8 fp8x8_scaled(uint32_t w0, uint32_t w1, float s
   const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
-// Eight e4m3 bytes from eight different rows -> bf16, each times its own row's scale.
-__device__ __forceinline__ bf16x8 fp8x8_rowscaled(uint32_t w0, uint32_t w1, const float (&sc)[8]) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
-  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
-  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
-  return bf16x8{(__bf16)(a[0] * sc[0]), (__bf16)(a[1] * sc[1]), (__bf16)(b[0] * sc[2]), (__bf16)(b[1] * sc[3]),
-                (__bf16)(c[0] * sc[4]), (__bf16)(c[1] * sc[5]), (__bf16)(d[0] * sc[6]), (__bf16)(d[1] * sc[7])};
-}
 // fp8 latent region: 512-byte rows, 16-byte chunk c of row r stored at chunk c ^ swz_n(r). Keeps
-// the K-operand reads (16 consecutive rows) and the transposed V reads (rows 4g..4g+3 and
-// 16+4g..16+4g+3) free of bank conflicts.
+// the K-operand reads (16 consecutive rows) free of bank conflicts.
 __device__ __forceinline__ int swz_n(int row) { return (row & 15) ^ ((row >> 4) << 3); }
-
-__device__ __forceinline__ bf16x8 lds_read_tr8_nz(LDS_AS uint32_t* __restrict__ p) {
-  typedef __attribute__((ext_vector_type(2))) int i32x2;
-  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<LDS_AS i32x2*>(p));
-  return __builtin_bit_cast(bf16x8, u32x4{(uint32_t)v[0], (uint32_t)v[1], 0u, 0u});
-}
 
 __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
   uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
@@ -785,18 +769,6 @@ __device__ __forceinline__ void mfma_sq2_cvt_last(f32x4& c0, f32x4& c1, const bf
       : "+v"(c0), "+v"(c1)
       : "v"(a0), "v"(a1), "a"(b));
 }
-__device__ __forceinline__ void mfma_o4_cvt(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& c3, const bf16x8& a,
-                                            const bf16x8& b0, const bf16x8& b1, const bf16x8& b2,
-                                            const bf16x8& b3) {
-  asm volatile(
-      "s_nop 2\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %4, %5, %0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %4, %6, %1\n\t"
-      "v_mfma_f32_16x16x32_bf16 %2, %4, %7, %2\n\t"
-      "v_mfma_f32_16x16x32_bf16 %3, %4, %8, %3"
-      : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
-      : "v"(a), "v"(b0), "v"(b1), "v"(b2), "v"(b3));
-}
 template <int N>
 __device__ __forceinline__ void mfma_drain_acc(f32x4 (&o)[N][4]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" ::: "memory");
@@ -845,7 +817,12 @@ struct Spec64 {
   static constexpr uint32_t kLOff = kMOff + 16;            // final l [64], then m [64]
   static constexpr uint32_t kRiOff = kLOff + 512;          // per value wave: block-table entries
   static constexpr int kRiWave = 4 * 32 + 8 * 32;          //   [4][8], index entries [8][8]
-  static constexpr int LDS = kRiOff + 4 * kRiWave;
+  // fp8 rows: V of a step dequantised to bf16 by the score waves (which convert those values for
+  // QK^T anyway), [2 steps][32 rows][1056 B], read by the value waves as bf16 slots are
+  static constexpr uint32_t kVOff = (kRiOff + 4 * kRiWave + 255) / 256 * 256;
+  static constexpr uint32_t kVBuf = kRows * kRowStrideA;
+  static constexpr int LDS = FP8 ? kVOff + 2 * kVBuf : kRiOff + 4 * kRiWave;
+  static_assert(LDS <= 160 * 1024, "LDS of one workgroup");
   static constexpr int kDmaOps = FP8 ? 6 : 8 + (HAS_B ? 1 : 0);  // row LDS-DMA instructions per bundle
 
   const DecodeArgs& a;
@@ -1044,6 +1021,13 @@ struct Spec64 {
           const bf16x8 k0 = k_operand(ka[ks % D][0], 0, ks);
           const bf16x8 k1 = k_operand(ka[ks % D][1], 1, ks);
           if constexpr (FP8) {
+            // the value columns of these operands, dequantised: score wave w stores k steps
+            // ks = w mod 4 into the step's V tile
+            if (32 * ks < kDv && (ks & 3) == wave) {
+              const uint32_t vt = kVOff + (t & 1) * kVBuf + 2 * (32 * ks + 8 * gl);
+              *reinterpret_cast<LDS_AS bf16x8*>(sm + vt + nl * kRowStrideA) = k0;
+              *reinterpret_cast<LDS_AS bf16x8*>(sm + vt + (16 + nl) * kRowStrideA) = k1;
+            }
             if (ks == KS - 1) mfma_sq2_cvt_last(sacc[0], sacc[1], k0, k1, qr[ks]);
             else if (ks == 0) mfma_sq2_cvt0(sacc[0], sacc[1], k0, k1, qr[0]);
             else mfma_sq2_cvt(sacc[0], sacc[1], k0, k1, qr[ks]);
@@ -1210,86 +1194,26 @@ struct Spec64 {
         __builtin_assume(vw >= 0 && vw < 4);
         // fp8 rows: scale bytes of the lane's eight KV rows, for the wave's two column groups
         // (group 2 vw for tiles 0..3, 2 vw + 1 for tiles 4..7), read as needed
-        uint32_t vsb[8];
-        float vsc[8];
-        auto v_scale_bytes = [&](int grp) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int row = (e < 4) ? 4 * gl + e : 12 + 4 * gl + e;
-            vsb[e] = *reinterpret_cast<const LDS_AS uint8_t*>(sm + su + kScOff + 8 * row + 2 * vw + grp);
-          }
-        };
-        if constexpr (FP8) v_scale_bytes(0);
-        // fp8 latent tile dt of this wave: chunk 8 vw + dt of eight rows; with the row swizzle
-        // (8 vw + dt) ^ f = 8 (vw ^ (f >> 3)) + (dt ^ (f & 7)), so the lane's address is one base
-        // XOR 16 dt
-        uint32_t vb8 = 0;
-        if constexpr (FP8) {
-          const int e = nl >> 1;
-          const int row = (e < 4) ? 4 * gl + e : 12 + 4 * gl + e;
-          const int f = swz_n(row);
-          vb8 = (uint32_t)(row * 512 + 128 * (vw ^ (f >> 3)) + 8 * (nl & 1)) | (uint32_t)(16 * (f & 7));
-          vb8 += su;  // the slot base has no bits below 256, so the XOR below stays within the row
-        }
-        // raw V operand: eight fp8 bytes (DSV3 rows), or room for a bf16 RoPE tile (DSV4 rows)
-        using VRaw = typename std::conditional<FP8, typename std::conditional<(kNope >= 512), u32x2, u32x4>::type,
-                                               bf16x8>::type;
-        auto v_raw = [&](int dt) -> VRaw {
+        // V^T operand of output tile dt: bf16 rows of the step's slot, or for fp8 rows of its V
+        // tile (dequantised by the score waves in step u)
+        const uint32_t vbase = FP8 ? kVOff + (u & 1) * kVBuf : su;
+        auto v_raw = [&](int dt) -> bf16x8 {
           const int col0 = 128 * vw + 16 * dt;  // first output column of the tile
-          if constexpr (FP8) {
-            if (col0 < kNope) {
-              const u32x4 w = __builtin_bit_cast(u32x4, lds_read_tr8_nz(reinterpret_cast<LDS_AS uint32_t*>(sm + (vb8 ^ (16u * dt)))));
-              if constexpr (kNope >= 512) return u32x2{w[0], w[1]};
-              else return w;
-            }
-            // DSV4 rows: columns past the fp8 values are the RoPE tail (bf16)
-            const int row = 4 * gl + (nl >> 2);
-            const int c = 2 * ((col0 - kNope) >> 4) + ((nl & 3) >> 1);
-            const uint32_t ad = su + kSlotA + 16 * (c ^ swz_b(row)) + 8 * (nl & 1);
-            const int c2 = c ^ swz_b(row + 16);
-            const bf16x4 v0 = lds_read_tr(sm, ad + row * 128);
-            const bf16x4 v1 = lds_read_tr(sm, su + kSlotA + (row + 16) * 128 + 16 * c2 + 8 * (nl & 1));
-            if constexpr (kNope >= 512) return VRaw{0u, 0u};  // not reached: every column is fp8
-            else return __builtin_bit_cast(u32x4, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-          } else {
-            const uint32_t ad = su + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (lane & 3) + 2 * col0;
-            const bf16x4 v0 = lds_read_tr(sm, ad);
-            const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
-            return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
+          const uint32_t ad = vbase + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (lane & 3) + 2 * col0;
+          const bf16x4 v0 = lds_read_tr(sm, ad);
+          const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
+          return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         };
-        auto v_operand = [&](const VRaw& raw, int dt) -> bf16x8 {
-          if constexpr (FP8) {
-            if (128 * vw + 16 * dt < kNope) return fp8x8_rowscaled(raw[0], raw[1], vsc);
-            if constexpr (kNope >= 512) return bf16x8{};  // not reached
-            else return __builtin_bit_cast(bf16x8, raw);
-          } else {
-            return raw;
-          }
-        };
-        // V operand tiles in flight: three for bf16 rows, two for fp8 rows (whose conversion
-        // already covers part of the read latency)
-        constexpr int VD = FP8 ? 2 : 3;
-        VRaw va[VD];
+        // V operand tiles in flight
+        constexpr int VD = 3;
+        bf16x8 va[VD];
 #pragma unroll
         for (int i = 0; i < VD - 1; ++i) va[i] = v_raw(i);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           if (dt + VD - 1 < 8) va[(dt + VD - 1) % VD] = v_raw(dt + VD - 1);
-          if constexpr (FP8) {
-            if (dt == 0 || dt == 4) {
 #pragma unroll
-              for (int e = 0; e < 8; ++e) vsc[e] = ue8m0_f32(vsb[e]);
-            }
-            if (dt == 1) v_scale_bytes(1);
-          }
-          const bf16x8 vop = v_operand(va[dt % VD], dt);
-          if constexpr (FP8) {
-            mfma_o4_cvt(o[dt][0], o[dt][1], o[dt][2], o[dt][3], vop, pb[0], pb[1], pb[2], pb[3]);
-          } else {
-#pragma unroll
-            for (int ht = 0; ht < 4; ++ht) mfma_o(o[dt][ht], vop, pb[ht]);
-          }
+          for (int ht = 0; ht < 4; ++ht) mfma_o(o[dt][ht], va[dt % VD], pb[ht]);
         }
       }
       if constexpr (FP8) bundle(t + 2);
