@@ -17,6 +17,7 @@ Everything is computed in float64 with numpy on dense, unpaged rows:
 - absorb.py    per-head weight absorption before (W_UK) and up-projection after (W_UV) the decode
 - swa_runs.py  sliding windows of cache slots compressed into at most two runs per token
 - gather.py    context rows of a chunk of requests gathered into a dense workspace
+- chunks.py    packing requests' context rows into workspace-sized chunks (host plan)
 
 Parity status of each function is stated in its module docstring.
 """
