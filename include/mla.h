@@ -29,7 +29,8 @@
  *
  * and, for the chunked-context prefill, the gather of context rows into a bf16 workspace:
  *
- *   mla_gather_context  rows of the requests of one context chunk, widened to bf16
+ *   mla_plan_context_chunks  (host) the requests' context rows packed into workspace chunks
+ *   mla_gather_context       rows of the requests of one context chunk, widened to bf16
  *
  * Conventions shared by every call
  * - All pointers are device pointers unless a parameter says "host". The caller owns every buffer;
@@ -202,6 +203,28 @@ int mla_v_up(int32_t tokens, int32_t num_heads, int32_t d_latent, int32_t d_v, c
 int mla_swa_runs(int32_t tokens, int32_t topk, const int32_t* kv_indices,
                  const int32_t* topk_lengths, int32_t page_size, int32_t kv_run_step, int32_t* runs,
                  void* stream);
+
+/* Chunked-context plan, on the host (vLLM mla_attention.py module docstring, the chunked prefill
+ * approach: the context rows are gathered in chunks of at most W workspace rows; requests are packed
+ * in order, the next request split on an aligned boundary when needed to fill W, so a chunk covers
+ * a contiguous run of requests and no empty span). A chunk takes whole remainders of requests while
+ * they fit; when the next does not, it takes that remainder's longest prefix that fits and whose
+ * length is a multiple of `alignment`, then closes. Requests without context rows are in no chunk.
+ *   num_reqs, context_lens (host int32 [num_reqs]; values < 0 count as 0)
+ *   workspace_rows W >= alignment >= 1 (e.g. page_size, so that every span starts page-aligned)
+ *   max_chunks, max_spans   capacities of the outputs (num_reqs + total / (W - W mod alignment) + 1
+ *                           chunks and num_reqs + chunks spans suffice)
+ *   num_chunks (host out); chunk_ptr (host out, [num_chunks + 1]): the spans of chunk c are
+ *   [chunk_ptr[c], chunk_ptr[c + 1]); span_req, span_start, span_len (host out): request, first
+ *   context row and rows of each span, in request order (a chunk's requests are a run of the
+ *   requests without the empty ones). A chunk's spans map to one mla_gather_context call:
+ *   num_reqs = its span count, block_table = the block-table rows of the spans' requests in span
+ *   order, seq_starts = span_start, cu_seq_lens = prefix sums of span_len.
+ * Returns MLA_ERR_SHAPE for invalid sizes, MLA_ERR_WORKSPACE if a capacity is exceeded. */
+int mla_plan_context_chunks(int32_t num_reqs, const int32_t* context_lens, int64_t workspace_rows,
+                            int32_t alignment, int32_t max_chunks, int32_t max_spans,
+                            int32_t* num_chunks, int32_t* chunk_ptr, int32_t* span_req,
+                            int32_t* span_start, int32_t* span_len);
 
 /* Context gather (vLLM mla_attention.py _compute_prefill_context: gather_and_maybe_dequant_cache
  * with cu_seq_lens, token_to_seq and seq_starts): output row i is row

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import MLA_KV_BF16, MLA_KV_FP8, MLAError, Problem  # noqa: F401
 
 __all__ = ["Problem", "make_problem", "workspace_size", "mla_decode_plan", "mla_decode",
-           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "MLADecode", "device_num_cus",
+           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "plan_context_chunks", "MLADecode", "device_num_cus",
            "MLAError"]
 
 
@@ -188,6 +188,27 @@ def mla_gather_context(p: Problem, block_table: torch.Tensor, cu_seq_lens: torch
         _ptr(cu_seq_lens, torch.int32, "cu_seq_lens"), _ptr(seq_starts, torch.int32, "seq_starts"),
         _ptr(token_to_seq, torch.int32, "token_to_seq"), kv_cache.data_ptr(),
         _ptr(dst, torch.bfloat16, "dst"), _stream(stream)))
+
+
+def plan_context_chunks(context_lens, workspace_rows: int, alignment: int):
+    """Host plan of the chunked-context gather: a list of chunks, each a list of
+    (request, first row, rows) spans (mla_plan_context_chunks)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    R = int(lens.size)
+    total = int(np.maximum(lens, 0).sum())
+    max_chunks = total // max(1, workspace_rows // alignment * alignment) + R + 2
+    max_spans = R + max_chunks
+    chunk_ptr = np.zeros(max_chunks + 1, dtype=np.int32)
+    req, start, ln = (np.zeros(max_spans, dtype=np.int32) for _ in range(3))
+    nc = np.zeros(1, dtype=np.int32)
+    lib = _lib.load()
+    addr = lambda a: a.ctypes.data
+    _lib.check("mla_plan_context_chunks", lib.mla_plan_context_chunks(
+        R, addr(lens) if R else None, int(workspace_rows), int(alignment), max_chunks, max_spans,
+        addr(nc), addr(chunk_ptr), addr(req), addr(start), addr(ln)))
+    return [[(int(req[k]), int(start[k]), int(ln[k])) for k in range(chunk_ptr[c], chunk_ptr[c + 1])]
+            for c in range(int(nc[0]))]
 
 
 class MLADecode:

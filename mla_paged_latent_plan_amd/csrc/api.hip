@@ -344,6 +344,61 @@ int mla_gather_context(const mla_problem* p, int32_t num_reqs, int64_t num_rows,
   a.ps_log2 = sh.ps_log2;
   return launch_rc(mla::launch_gather(a, sh.fmt, sh.d_qk, static_cast<hipStream_t>(stream)));
 }
+int mla_plan_context_chunks(int32_t num_reqs, const int32_t* context_lens, int64_t workspace_rows,
+                            int32_t alignment, int32_t max_chunks, int32_t max_spans,
+                            int32_t* num_chunks, int32_t* chunk_ptr, int32_t* span_req,
+                            int32_t* span_start, int32_t* span_len) {
+  if (num_reqs < 0 || alignment < 1 || workspace_rows < alignment || max_chunks < 0 ||
+      max_spans < 0)
+    return MLA_ERR_SHAPE;
+  if (num_chunks == nullptr || chunk_ptr == nullptr || (num_reqs > 0 && context_lens == nullptr))
+    return MLA_ERR_NULL;
+  int32_t nc = 0, ns = 0;
+  int64_t rows = 0;  // rows of the open chunk
+  chunk_ptr[0] = 0;
+  auto add_span = [&](int32_t r, int64_t start, int64_t len) -> bool {
+    if (ns >= max_spans || span_req == nullptr || span_start == nullptr || span_len == nullptr)
+      return false;
+    span_req[ns] = r;
+    span_start[ns] = (int32_t)start;
+    span_len[ns] = (int32_t)len;
+    ++ns;
+    rows += len;
+    return true;
+  };
+  auto close_chunk = [&]() -> bool {
+    if (nc >= max_chunks) return false;
+    chunk_ptr[++nc] = ns;
+    rows = 0;
+    return true;
+  };
+  int64_t s = 0;  // first row of what remains of request r
+  for (int32_t r = 0; r < num_reqs;) {
+    const int64_t remaining = (int64_t)(context_lens[r] > 0 ? context_lens[r] : 0) - s;
+    if (remaining <= 0) {
+      ++r;
+      s = 0;
+      continue;
+    }
+    if (rows + remaining <= workspace_rows) {  // the whole remainder fits
+      if (!add_span(r, s, remaining)) return MLA_ERR_WORKSPACE;
+      ++r;
+      s = 0;
+      if (rows == workspace_rows && !close_chunk()) return MLA_ERR_WORKSPACE;
+      continue;
+    }
+    // the longest aligned prefix that fits, then the chunk is closed
+    const int64_t take = (workspace_rows - rows) / alignment * alignment;
+    if (take > 0) {
+      if (!add_span(r, s, take)) return MLA_ERR_WORKSPACE;
+      s += take;
+    }
+    if (!close_chunk()) return MLA_ERR_WORKSPACE;
+  }
+  if (rows > 0 && !close_chunk()) return MLA_ERR_WORKSPACE;
+  *num_chunks = nc;
+  return MLA_OK;
+}
 const char* mla_strerror(int status) {
   switch (status) {
     case MLA_OK: return "ok";

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from conftest import ROOT
@@ -187,3 +188,12 @@ def test_gather_host_checks(lib):
                                   vp(4096), vp(4096), None) == 1
     assert lib.mla_gather_context(ctypes.byref(p), 1, i64(4), vp(4096), vp(4096), None, vp(4096),
                                   vp(4096), vp(4100), None) == 7
+
+
+def test_planner_null_and_empty(lib):
+    nc = np.zeros(1, dtype=np.int32)
+    ptr = np.zeros(4, dtype=np.int32)
+    assert lib.mla_plan_context_chunks(0, None, 64, 16, 4, 4, nc.ctypes.data, ptr.ctypes.data,
+                                       None, None, None) == 0 and nc[0] == 0
+    assert lib.mla_plan_context_chunks(2, None, 64, 16, 4, 4, nc.ctypes.data, ptr.ctypes.data,
+                                       None, None, None) == 1
