@@ -62,6 +62,12 @@ CASES = {
     "fp8_sparse_h128": (Spec("fp8_sparse_h128", batch=2, q_len=1, num_heads=128, page_size=64,
                              kv_format="fp8", seqlens=(5000, 3), topk=300, sm_scale=S, seed=35),
                         None),
+    # a sink with empty contexts: O = 0 and LSE = the sink logit for those requests
+    "sink_empty": (Spec("sink_empty", batch=4, q_len=1, num_heads=16, page_size=16,
+                        seqlens=(0, 5, 0, 300), sink=True, sm_scale=S, seed=36), None),
+    "fp8_h128_sink_empty": (Spec("fp8_h128_sink_empty", batch=3, q_len=1, num_heads=128,
+                                 page_size=64, kv_format="fp8", seqlens=(0, 700, 0), sink=True,
+                                 sm_scale=S, seed=37), None),
 }
 
 
@@ -236,3 +242,28 @@ def test_maximum_sizes(case):
     H.assert_parity(m, ctx=case)
     want = H.plan_words(wl, used)
     assert np.array_equal(plan.view(torch.int32).numpy()[:len(want)], want)
+
+
+def test_sparse_duplicate_indices_count_per_occurrence():
+    """Index lists with repeated entries: each occurrence is one more term of the softmax (the
+    oracle's reading), so a list holding every index twice gives the same O as once and an LSE
+    larger by ln 2."""
+    spec = Spec("dup_idx", batch=2, q_len=1, num_heads=16, page_size=16, seqlens=(300, 90),
+                topk=128, sm_scale=S, seed=38)
+    wl = make(spec)
+    idx = wl.indices.numpy().copy()
+    idx[:, :, 64:] = idx[:, :, :64]  # entries 64..127 repeat entries 0..63
+    wl.indices = torch.from_numpy(idx)
+    print("[gpu] duplicate indices", flush=True)
+    out, lse, _, _ = H.run_gpu(wl)
+    O, L, A = H.oracle_of(wl, abs_mass=True)
+    m = H.metrics(out, lse, O, L, A)
+    print(f"[gpu]   {m}", flush=True)
+    H.assert_parity(m, ctx="duplicate indices")
+    half = dataclasses.replace(spec, topk=64, name="dup_idx_half")
+    wl2 = make(half)
+    wl2.indices = torch.from_numpy(np.ascontiguousarray(idx[:, :, :64]))
+    out2, lse2, _, _ = H.run_gpu(wl2)
+    np.testing.assert_allclose(lse.numpy(), lse2.numpy() + math.log(2.0), atol=1e-4)
+    np.testing.assert_allclose(out.to(torch.float64).numpy(), out2.to(torch.float64).numpy(),
+                               atol=2e-2)
