@@ -6,8 +6,11 @@ Each timed step is preceded (outside its events) by a read-only sweep over a 1 G
 was written once at set-up: it evicts the KV cache's lines from the 256 MB Infinity Cache and
 leaves only clean lines there, so the decode reads the KV cache from HBM without also paying for
 the write-back of an evicting kernel's dirty lines (a write fill of the same size is kept as an
-option, --flush write). Warm back-to-back figures are reported separately, eager and as a replayed
-HIP graph of the same steps. Prints one JSON line.
+option, --flush write). The step time (ms_per_step, value) brackets decode + combine with one pair
+of events; a second loop with an event between the two kernels gives the per-kernel split
+(decode_ms, combine_ms) and the decode time the roofline uses — that middle event record delays the
+combine's dispatch, so the split sums to more than the step. Warm back-to-back figures are reported
+separately, eager and as a replayed HIP graph of the same steps. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|1|3|4|5|s1|s4] [--no-cpu]
 """
@@ -624,7 +627,19 @@ def main():
     wall = (time.perf_counter() - t0) / K * 1e3
     dec_ms = np.array([a.elapsed_time(m) for a, m, _ in evs])
     com_ms = np.array([m.elapsed_time(e) for _, m, e in evs])
-    step_ms = dec_ms + com_ms
+    # the step itself, timed without the marker between the two kernels (the loop above gives the
+    # per-kernel split; its middle event record can delay the combine's dispatch)
+    sevs = [(ev(), ev()) for _ in range(K)]
+    for k in range(K):
+        if not args.no_flush:
+            evict(k)
+        a, e = sevs[k]
+        a.record(stream)
+        decode()
+        combine()
+        e.record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([a.elapsed_time(e) for a, e in sevs])
 
     # warm back-to-back (cache-resident) for context
     wa, wb = ev(), ev()
@@ -708,6 +723,7 @@ def main():
         "decode_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 4),
                               round(float(np.percentile(dec_ms, 90)), 4)],
         "combine_ms": round(float(com_ms.mean()), 4),
+        "decode_plus_combine_ms_with_marker": round(float((dec_ms + com_ms).mean()), 4),
         "plan_ms": round(plan_ms, 4),
         "warm_ms_per_step": round(warm_ms, 4),
         "graph_warm_ms_per_step": round(graph_ms, 4),
