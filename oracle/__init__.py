@@ -18,6 +18,8 @@ Everything is computed in float64 with numpy on dense, unpaged rows:
 - swa_runs.py  sliding windows of cache slots compressed into at most two runs per token
 - gather.py    context rows of a chunk of requests gathered into a dense workspace
 - chunks.py    packing requests' context rows into workspace-sized chunks (host plan)
+- sparse_prefill.py  prefill tokens attending over their own index lists into a flat buffer,
+                with the per-row maximum logit
 
 Parity status of each function is stated in its module docstring.
 """
