@@ -32,6 +32,10 @@
  *   mla_plan_context_chunks  (host) the requests' context rows packed into workspace chunks
  *   mla_gather_context       rows of the requests of one context chunk, widened to bf16
  *
+ * and the sparse prefill over index lists into a flat latent buffer, with each row's max logit:
+ *
+ *   mla_sparse_prefill       plan, decode and combine of the prefill tokens in one call
+ *
  * Conventions shared by every call
  * - All pointers are device pointers unless a parameter says "host". The caller owns every buffer;
  *   the library never allocates, frees or synchronises. `stream` is a hipStream_t (NULL = default
@@ -245,6 +249,33 @@ int mla_gather_context(const mla_problem* p, int32_t num_reqs, int64_t num_rows,
                        const int32_t* block_table, const int32_t* cu_seq_lens,
                        const int32_t* seq_starts, const int32_t* token_to_seq, const void* kv_cache,
                        void* dst, void* stream);
+
+/* Sparse prefill (FlashMLA wrapper, flash_mla_sparse_fwd(q, kv, indices, sm_scale, d_v = 512)
+ * returning out, max_logits and lse): each of s_q prefill tokens attends, with all of its heads,
+ * over the rows of one flat latent buffer that its own index list names. For token t and head h,
+ * over the entries j of indices[t, :] in [0, s_kv) (repeats count once per occurrence):
+ *   s_j = sm_scale * <q[t, h, :], kv[j, :]>,  max_logits = max s_j,  LSE = ln sum exp(s_j),
+ *   out = sum exp(s_j - LSE) kv[j, 0:512];  no valid entry: out = 0, max_logits = LSE = -inf.
+ *   s_q          1 <= s_q <= 8192 query tokens (larger prefills are issued in several calls)
+ *   num_heads    H >= 1 query heads; every head of a token reads each gathered row once per
+ *                64-head tile
+ *   d_qk         576 (DeepSeek-V3: 512 latent + 64 RoPE) or 512 (V4)
+ *   topk         >= 1 index entries per token; s_kv: 1 <= rows of kv <= INT32_MAX
+ *   q            bf16 [s_q, H, d_qk]; kv bf16 [s_kv, d_qk] contiguous (one latent KV head)
+ *   indices      int32 [s_q, topk]; entries outside [0, s_kv) (-1 padding) name no row
+ *   workspace    at least mla_sparse_prefill_workspace_size bytes, 16-byte aligned, owned by the
+ *                caller; it holds the request metadata, the plan and the split partials
+ *   out          bf16 [s_q, H, 512]; max_logits and lse fp32 [H, s_q] (the decode's LSE layout
+ *                [B, H, Sq] with one batch), natural-log units of the scaled scores
+ * The call enqueues a metadata fill, mla_decode_plan, mla_decode and mla_combine on `stream`; it
+ * runs the prefill as one request of q_len = s_q tokens whose positions are kv's rows (pages of
+ * 4096 rows, page i at page i). q, kv, workspace and out 16-byte aligned. */
+int mla_sparse_prefill_workspace_size(int32_t s_q, int32_t num_heads, int32_t d_qk, int32_t topk,
+                                      int64_t s_kv, int32_t num_cus, size_t* workspace_bytes);
+int mla_sparse_prefill(int32_t s_q, int32_t num_heads, int32_t d_qk, int32_t topk, int64_t s_kv,
+                       int32_t num_cus, const void* q, const void* kv, const int32_t* indices,
+                       float sm_scale, void* workspace, size_t workspace_bytes, void* out,
+                       float* max_logits, float* lse, void* stream);
 
 /* Static description of a status code. */
 const char* mla_strerror(int status);

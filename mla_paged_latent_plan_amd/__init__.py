@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import MLA_KV_BF16, MLA_KV_FP8, MLAError, Problem  # noqa: F401
 
 __all__ = ["Problem", "make_problem", "workspace_size", "mla_decode_plan", "mla_decode",
-           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "plan_context_chunks", "MLADecode", "device_num_cus",
+           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "plan_context_chunks",
+           "sparse_prefill_workspace_size", "mla_sparse_prefill", "MLADecode", "device_num_cus",
            "MLAError"]
 
 
@@ -188,6 +189,42 @@ def mla_gather_context(p: Problem, block_table: torch.Tensor, cu_seq_lens: torch
         _ptr(cu_seq_lens, torch.int32, "cu_seq_lens"), _ptr(seq_starts, torch.int32, "seq_starts"),
         _ptr(token_to_seq, torch.int32, "token_to_seq"), kv_cache.data_ptr(),
         _ptr(dst, torch.bfloat16, "dst"), _stream(stream)))
+
+
+def sparse_prefill_workspace_size(s_q: int, num_heads: int, d_qk: int, topk: int, s_kv: int,
+                                  num_cus: int) -> int:
+    """Workspace bytes of mla_sparse_prefill for these sizes."""
+    import ctypes
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    _lib.check("mla_sparse_prefill_workspace_size", lib.mla_sparse_prefill_workspace_size(
+        int(s_q), int(num_heads), int(d_qk), int(topk), int(s_kv), int(num_cus), ctypes.byref(n)))
+    return n.value
+
+
+def mla_sparse_prefill(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale: float,
+                       workspace: torch.Tensor, out: torch.Tensor, max_logits: torch.Tensor,
+                       lse: torch.Tensor, num_cus: int, stream=None) -> None:
+    """q [s_q, H, d_qk], kv [s_kv, d_qk] bf16, indices int32 [s_q, topk] -> out bf16 [s_q, H, 512],
+    max_logits and lse fp32 [H, s_q] (flash_mla_sparse_fwd's outputs)."""
+    lib = _lib.load()
+    s_q, H, d_qk = q.shape
+    s_kv = int(kv.shape[0])
+    if kv.dim() != 2 or int(kv.shape[1]) != d_qk:
+        raise ValueError(f"kv must be [s_kv, {d_qk}]")
+    if indices.dim() != 2 or int(indices.shape[0]) != s_q:
+        raise ValueError(f"indices must be [{s_q}, topk]")
+    topk = int(indices.shape[1])
+    if tuple(out.shape) != (s_q, H, 512) or tuple(max_logits.shape) != (H, s_q) or \
+            tuple(lse.shape) != (H, s_q):
+        raise ValueError("out must be [s_q, H, 512], max_logits and lse [H, s_q]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _lib.check("mla_sparse_prefill", lib.mla_sparse_prefill(
+        s_q, H, d_qk, topk, s_kv, int(num_cus), _ptr(q, torch.bfloat16, "q"),
+        _ptr(kv, torch.bfloat16, "kv"), _ptr(indices, torch.int32, "indices"), float(sm_scale),
+        _ptr(workspace, workspace.dtype, "workspace"), ws_bytes, _ptr(out, torch.bfloat16, "out"),
+        _ptr(max_logits, torch.float32, "max_logits"), _ptr(lse, torch.float32, "lse"),
+        _stream(stream)))
 
 
 def plan_context_chunks(context_lens, workspace_rows: int, alignment: int):

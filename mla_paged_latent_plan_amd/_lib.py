@@ -22,7 +22,8 @@ STATUS = {
 }
 
 EXPORTS = ("mla_get_workspace_size", "mla_device_num_cus", "mla_decode_plan", "mla_decode",
-           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "mla_plan_context_chunks", "mla_strerror")
+           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "mla_plan_context_chunks",
+           "mla_sparse_prefill_workspace_size", "mla_sparse_prefill", "mla_strerror")
 
 
 class MLAError(RuntimeError):
@@ -78,6 +79,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_gather_context.argtypes = [P, i32, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp]
     lib.mla_plan_context_chunks.argtypes = [i32, vp, ctypes.c_int64, i32, i32, i32, vp, vp, vp, vp,
                                             vp]
+    i64 = ctypes.c_int64
+    lib.mla_sparse_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i64, i32,
+                                                      ctypes.POINTER(sz)]
+    lib.mla_sparse_prefill.argtypes = [i32, i32, i32, i32, i64, i32, vp, vp, vp, ctypes.c_float,
+                                       vp, sz, vp, vp, vp, vp]
     lib.mla_strerror.argtypes = [ctypes.c_int]
     lib.mla_strerror.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:

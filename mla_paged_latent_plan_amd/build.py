@@ -10,7 +10,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
-SOURCES = ["plan.hip", "decode.hip", "combine.hip", "kvwrite.hip", "absorb.hip", "swa_runs.hip", "gather.hip", "api.hip"]
+SOURCES = ["plan.hip", "decode.hip", "combine.hip", "kvwrite.hip", "absorb.hip", "swa_runs.hip", "gather.hip", "sparse_meta.hip", "api.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -131,10 +131,17 @@ int mla_decode_plan(const mla_problem* p, int32_t num_cus, const int32_t* seqlen
   return launch_rc(mla::launch_plan(a, static_cast<hipStream_t>(stream)));
 }
 
-int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void* kv_cache,
-               const int32_t* block_table, const int32_t* seqlens, float sm_scale,
-               const int32_t* indices, const float* sink, const void* plan, void* partials,
-               size_t partial_bytes, void* out, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// mla_decode with an optional per-row maximum (max_logits, with part_max holding S_max * R floats
+// for the split rows).
+int decode_impl(const mla_problem* p, int32_t num_cus, const void* q, const void* kv_cache,
+                const int32_t* block_table, const int32_t* seqlens, float sm_scale,
+                const int32_t* indices, const float* sink, const void* plan, void* partials,
+                size_t partial_bytes, void* out, float* lse, float* max_logits, float* part_max,
+                void* stream) {
   Shape sh;
   int rc = derive(p, num_cus, &sh);
   if (rc != MLA_OK) return rc;
@@ -162,6 +169,8 @@ int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void*
   a.part_lse = reinterpret_cast<float*>(a.part_o + (size_t)sh.s_max * sh.R * mla::kDv);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
+  a.max_logits = max_logits;
+  a.part_max = part_max;
   a.page_stride = sh.page_stride;
   a.num_pages = sh.num_pages;
   a.row_bytes = sh.row_bytes;
@@ -186,8 +195,9 @@ int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void*
   return launch_rc(mla::launch_decode(a, sh, static_cast<hipStream_t>(stream)));
 }
 
-int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const void* partials,
-                size_t partial_bytes, const float* sink, void* out, float* lse, void* stream) {
+int combine_impl(const mla_problem* p, int32_t num_cus, const void* plan, const void* partials,
+                 size_t partial_bytes, const float* sink, void* out, float* lse,
+                 const float* part_max, float* max_logits, void* stream) {
   Shape sh;
   int rc = derive(p, num_cus, &sh);
   if (rc != MLA_OK) return rc;
@@ -203,6 +213,8 @@ int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const v
   a.sink = sink;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
+  a.part_max = part_max;
+  a.max_logits = max_logits;
   a.grp_ptr_off = lay.grp_ptr;
   a.B = sh.B;
   a.Sq = sh.Sq;
@@ -211,6 +223,111 @@ int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const v
   a.G = sh.G;
   a.sparse = sh.topk > 0;
   return launch_rc(mla::launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// The sparse prefill as one request over the flat buffer: its positions are kv's rows, pages of
+// 4096 rows, page i at page i. Workspace: [s_kv, identity page table] | plan | partials | split
+// maxima, each part 256-byte aligned.
+struct SparseLayout {
+  mla_problem p;
+  Shape sh;
+  int32_t pages;
+  size_t plan_off, plan_bytes, part_off, part_bytes, max_off, bytes;
+};
+
+int sparse_layout(int32_t s_q, int32_t num_heads, int32_t d_qk, int32_t topk, int64_t s_kv,
+                  int32_t num_cus, SparseLayout* L) {
+  if (s_q < 1 || topk < 1 || s_kv < 1 || s_kv > INT32_MAX) return MLA_ERR_SHAPE;
+  constexpr int32_t kPage = 4096;
+  mla_problem& p = L->p;
+  p.batch = 1;
+  p.q_len = s_q;
+  p.num_heads = num_heads;
+  p.d_qk = d_qk;
+  p.d_v = 512;
+  p.d_rope = 64;
+  p.kv_format = MLA_KV_BF16;
+  p.page_size = kPage;
+  p.page_stride_bytes = (int64_t)kPage * 2 * d_qk;
+  p.num_pages = (s_kv + kPage - 1) / kPage;
+  p.max_pages_per_seq = (int32_t)p.num_pages;
+  p.topk = topk;
+  p.causal = 0;
+  p.window = 0;
+  int rc = derive(&p, num_cus, &L->sh);
+  if (rc != MLA_OK) return rc;
+  L->pages = (int32_t)p.num_pages;
+  L->plan_off = round256(sizeof(int32_t) * (1 + (size_t)L->pages));
+  L->plan_bytes = (size_t)PlanLayout::make(L->sh.G, L->sh.U).bytes;
+  L->part_off = round256(L->plan_off + L->plan_bytes);
+  L->part_bytes = partial_size(L->sh);
+  L->max_off = round256(L->part_off + L->part_bytes);
+  L->bytes = L->max_off + (size_t)L->sh.s_max * L->sh.R * sizeof(float);
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void* kv_cache,
+               const int32_t* block_table, const int32_t* seqlens, float sm_scale,
+               const int32_t* indices, const float* sink, const void* plan, void* partials,
+               size_t partial_bytes, void* out, float* lse, void* stream) {
+  return decode_impl(p, num_cus, q, kv_cache, block_table, seqlens, sm_scale, indices, sink, plan,
+                     partials, partial_bytes, out, lse, nullptr, nullptr, stream);
+}
+
+int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const void* partials,
+                size_t partial_bytes, const float* sink, void* out, float* lse, void* stream) {
+  return combine_impl(p, num_cus, plan, partials, partial_bytes, sink, out, lse, nullptr, nullptr,
+                      stream);
+}
+
+int mla_sparse_prefill_workspace_size(int32_t s_q, int32_t num_heads, int32_t d_qk, int32_t topk,
+                                      int64_t s_kv, int32_t num_cus, size_t* workspace_bytes) {
+  SparseLayout L;
+  int rc = sparse_layout(s_q, num_heads, d_qk, topk, s_kv, num_cus, &L);
+  if (rc != MLA_OK) return rc;
+  if (workspace_bytes) *workspace_bytes = L.bytes;
+  return MLA_OK;
+}
+
+int mla_sparse_prefill(int32_t s_q, int32_t num_heads, int32_t d_qk, int32_t topk, int64_t s_kv,
+                       int32_t num_cus, const void* q, const void* kv, const int32_t* indices,
+                       float sm_scale, void* workspace, size_t workspace_bytes, void* out,
+                       float* max_logits, float* lse, void* stream) {
+  SparseLayout L;
+  int rc = sparse_layout(s_q, num_heads, d_qk, topk, s_kv, num_cus, &L);
+  if (rc != MLA_OK) return rc;
+  if (q == nullptr || kv == nullptr || indices == nullptr || workspace == nullptr ||
+      out == nullptr || max_logits == nullptr || lse == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(workspace) || !aligned16(out))
+    return MLA_ERR_ALIGN;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return MLA_ERR_SHAPE;
+  if (workspace_bytes < L.bytes) return MLA_ERR_WORKSPACE;
+  if (num_cus <= 0) {
+    rc = query_cus(&num_cus);
+    if (rc != MLA_OK) return rc;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* meta = reinterpret_cast<int32_t*>(ws);
+  void* plan = ws + L.plan_off;
+  void* partials = ws + L.part_off;
+  float* part_max = reinterpret_cast<float*>(ws + L.max_off);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = launch_rc(mla::launch_sparse_meta(meta, (int32_t)s_kv, L.pages, st));
+  if (rc != MLA_OK) return rc;
+  rc = mla_decode_plan(&L.p, num_cus, meta, nullptr, plan, L.plan_bytes, stream);
+  if (rc != MLA_OK) return rc;
+  rc = decode_impl(&L.p, num_cus, q, kv, meta + 1, meta, sm_scale, indices, nullptr, plan,
+                   partials, L.part_bytes, out, lse, max_logits, part_max, stream);
+  if (rc != MLA_OK) return rc;
+  return combine_impl(&L.p, num_cus, plan, partials, L.part_bytes, nullptr, out, lse, part_max,
+                      max_logits, stream);
 }
 
 int mla_kv_write(const mla_problem* p, int64_t num_tokens, const void* kv_c, const void* k_pe,

@@ -6,7 +6,8 @@
 // LSE_i = -inf and no weight (vLLM neutralize_empty_context_partials). The sink (HALOps attn_sink)
 // then adds exp(sink_h) once to the denominator. A group with no splits at all gets O = 0 and
 // LSE = -inf, or LSE = sink_h with a sink. Groups with exactly one split were finished by
-// mla_decode and are skipped.
+// mla_decode and are skipped. On request the row's largest scaled score is the largest of its
+// splits' (-inf without splits).
 //
 // Launch: one workgroup of 256 threads per (group, 4 query rows); 64 threads per row, each
 // owning 8 consecutive columns, so bf16 partial rows are read as contiguous 1 KB lines. Lane i reads
@@ -139,6 +140,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   w.w = (uint32_t)f2bf(acc[6] * scale) | ((uint32_t)f2bf(acc[7] * scale) << 16);
   *reinterpret_cast<uint4*>(a.out + ((int64_t)g * a.R + r) * kDv + c) = w;
   if (lane == 0) a.lse[((int64_t)b * a.H + h) * a.Sq + t] = lse;
+  if (a.max_logits != nullptr) {
+    float pm = kNegInf;
+    for (int s = s0; s < s1; s += 64)
+      if (s + lane < s1) pm = fmaxf(pm, a.part_max[(int64_t)(s + lane) * a.R + r]);
+    pm = wave_max(pm);
+    if (lane == 0) a.max_logits[((int64_t)b * a.H + h) * a.Sq + t] = pm;
+  }
 }
 
 }  // namespace

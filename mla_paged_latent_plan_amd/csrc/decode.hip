@@ -4,7 +4,9 @@
 // all heads of a query group attend over the same latent rows, K = [kv_c, k_pe] (d_qk wide) and
 // V = kv_c (the first 512 columns). Per split (a run of 64-row blocks of one group, from the
 // plan) a workgroup produces either the final bf16 O and natural-log LSE, or a partial
-// (bf16 O normalised by its own denominator, fp32 LSE without the sink) for mla_combine.
+// (bf16 O normalised by its own denominator, fp32 LSE without the sink) for mla_combine. On
+// request the 64-row kernel also writes each row's largest scaled score (the max_logits output of
+// the FlashMLA wrapper's flash_mla_sparse_fwd), final or per split.
 //
 // Mapping onto CDNA4:
 // - Workgroup = 4 waves; the group's query rows (heads, times tokens when q_len > 1) are the
@@ -962,6 +964,7 @@ struct Spec64 {
     const int qpos = L - a.Sq + (sparse ? 0 : (qrow / a.H));
     const bool dense_mask = !sparse && (a.causal || a.window > 0);
     float m_ref = kNegInf, l_acc = 0.f;
+    float m_top = kNegInf;  // the row's true maximum (m_ref trails it by up to kTau)
     lds_barrier();  // prologue: step q0 landed
 
     for (int t = q0; t <= qend; ++t) {
@@ -1070,6 +1073,7 @@ struct Spec64 {
           for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kt][e]);
         mx = rows_max(mx);
         const float mnew = mx * a.scale_log2;  // -inf stays -inf (scale > 0)
+        m_top = fmaxf(m_top, mnew);
         const bool up = mnew > m_ref + kTau;
         float alpha = 1.f;
         if (up) {
@@ -1102,6 +1106,11 @@ struct Spec64 {
     if (gl == 0) {
       *reinterpret_cast<LDS_AS float*>(sm + kLOff + 4 * (wave * 16 + nl)) = lt;
       *reinterpret_cast<LDS_AS float*>(sm + kLOff + 256 + 4 * (wave * 16 + nl)) = m_ref;
+      if (a.max_logits != nullptr && qrow < a.R) {  // natural-log units of the scaled scores
+        const float ml = m_top * 0.69314718055994530942f;
+        if (nsplit == 1) a.max_logits[lse_index(qrow)] = ml;
+        else a.part_max[(int64_t)cur_split * a.R + qrow] = ml;
+      }
     }
     lds_barrier();  // statistics published
     lds_barrier();  // output rows staged
@@ -1363,8 +1372,10 @@ hipError_t launch_spec64(DecodeArgs a, hipStream_t s) {
 template <int DQK>
 hipError_t launch_dqk(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
   if (sh.fmt != 0) return launch_spec64<DQK, true>(a, s);  // fp8 rows: 64-row tiles for any R
-  if (sh.R <= 16) return launch_cfg<Cfg<16, 4, DQK>>(a, s);
-  if (sh.R <= 32) return launch_cfg<Cfg<16, 2, DQK>>(a, s);
+  if (a.max_logits == nullptr) {  // the per-row maximum is produced by the 64-row kernel only
+    if (sh.R <= 16) return launch_cfg<Cfg<16, 4, DQK>>(a, s);
+    if (sh.R <= 32) return launch_cfg<Cfg<16, 2, DQK>>(a, s);
+  }
   return launch_spec64<DQK, false>(a, s);
 }
 

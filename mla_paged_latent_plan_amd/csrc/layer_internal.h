@@ -1,5 +1,5 @@
 // Internal definitions of the kernels around the decode (absorption GEMMs, sliding-window run
-// plan, context gather) shared with the C-ABI layer.
+// plan, context gather, sparse prefill metadata) shared with the C-ABI layer.
 #pragma once
 
 #include "mla_internal.h"
@@ -41,5 +41,7 @@ struct GatherArgs {
 hipError_t launch_absorb_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int fmt, int d_qk, hipStream_t s);
 hipError_t launch_swa_runs(const SwaRunsArgs& a, hipStream_t s);
+// meta[0] = s_kv, meta[1 + i] = i for i < pages (pages >= 1).
+hipError_t launch_sparse_meta(int32_t* meta, int32_t s_kv, int32_t pages, hipStream_t s);
 
 }  // namespace mla

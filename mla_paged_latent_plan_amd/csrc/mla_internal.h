@@ -74,6 +74,8 @@ struct DecodeArgs {
   float* part_lse;
   uint16_t* out;
   float* lse;
+  float* max_logits;  // optional: per-row maximum scaled score (LSE layout), or nullptr
+  float* part_max;    // fp32 [S_max][R] per-split maxima; used only with max_logits
   int64_t page_stride, num_pages, row_bytes;
   int64_t scale_off;  // fp8 rows: byte offset of a page's scale slots (page_size * row_bytes)
   int64_t grp_ptr_off, unit_ptr_off, grp_rows_off, splits_off;
@@ -88,6 +90,8 @@ struct CombineArgs {
   const float* sink;
   uint16_t* out;
   float* lse;
+  const float* part_max;  // with max_logits: per-split maxima written by the decode
+  float* max_logits;      // optional, or nullptr
   int64_t grp_ptr_off;
   int B, Sq, H, R, G;
   int sparse;

@@ -197,3 +197,39 @@ def test_planner_null_and_empty(lib):
                                        None, None, None) == 0 and nc[0] == 0
     assert lib.mla_plan_context_chunks(2, None, 64, 16, 4, 4, nc.ctypes.data, ptr.ctypes.data,
                                        None, None, None) == 1
+
+
+def test_sparse_prefill_host_checks(lib):
+    """Workspace layout of the sparse prefill (metadata | plan | partials | split maxima, 256-byte
+    aligned parts) and its argument checks; no launch happens on any failing call."""
+    vp = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    n = ctypes.c_size_t(0)
+    s_q, H, d_qk, topk, s_kv, cus = 300, 128, 576, 2048, 70000, 256
+    assert lib.mla_sparse_prefill_workspace_size(s_q, H, d_qk, topk, i64(s_kv), cus, ctypes.byref(n)) == 0
+    pages = (s_kv + 4095) // 4096
+    p = mla.make_problem(1, s_q, H, d_qk, 0, 4096, 4096 * 2 * d_qk, pages, pages, topk=topk)
+    rc, plan_b, part_b = ws(p, cus)
+    assert rc == 0
+    r256 = lambda x: (x + 255) // 256 * 256
+    U = cus // ((H + 63) // 64)
+    expect = r256(r256(r256(4 * (1 + pages)) + plan_b) + part_b) + (s_q + U) * H * 4
+    assert n.value == expect
+    # sizes out of range
+    for args in ((0, H, d_qk, topk, 5), (8193, H, d_qk, topk, 5), (4, H, d_qk, 0, 5),
+                 (4, H, d_qk, topk, 0), (4, H, d_qk, topk, 2 ** 31), (4, H, 600, topk, 5),
+                 (4, 0, d_qk, topk, 5)):
+        assert lib.mla_sparse_prefill_workspace_size(*args[:4], i64(args[4]), cus, ctypes.byref(n)) == 2, args
+    # nulls, alignment, scale, workspace size
+    good_args = [4, 64, 512, 128, i64(1000), cus, vp(4096), vp(4096), vp(4096), 0.1, vp(4096),
+                 1 << 30, vp(4096), vp(4096), vp(4096), None]
+    def call(**change):
+        a = list(good_args)
+        for k, v in change.items():
+            a[int(k[1:])] = v
+        return lib.mla_sparse_prefill(*a)
+    assert call(a6=None) == 1 and call(a8=None) == 1 and call(a13=None) == 1
+    assert call(a10=None) == 1
+    assert call(a7=vp(4100)) == 7 and call(a12=vp(4104)) == 7
+    assert call(a9=0.0) == 2 and call(a9=float("nan")) == 2
+    assert call(a11=16) == 6

@@ -216,3 +216,59 @@ def make(spec: Spec, seqlens: Optional[np.ndarray] = None,
                     nope_codes=nope, scale_codes=scales, rope_bf16=rope,
                     cache=torch.from_numpy(cache), block_table=torch.from_numpy(block_table),
                     page_stride=stride, indices=indices, topk_lens=tl, sink=sink)
+
+
+# ---- sparse prefill (FlashMLA wrapper, flash_mla_sparse_fwd) ----------------------------------
+
+@dataclasses.dataclass
+class SparsePrefillSpec:
+    """Prefill tokens attending over index lists into one flat latent buffer kv [s_kv, d_qk].
+
+    Token t sits at position s_kv - s_q + t (the prefill's tokens are the buffer's last rows) and
+    lists topk rows of its causal prefix [0, pos_t]: the whole prefix, padded with -1, when it has
+    at most topk rows, else topk distinct rows spread over it (a sorted uniform draw, columns then
+    shuffled by one permutation shared by all tokens). `invalid_frac` of the remaining entries are
+    replaced by -1 or by rows past s_kv, and the first `empty_tokens` tokens list no valid row.
+    """
+    name: str
+    s_q: int
+    num_heads: int
+    s_kv: int
+    topk: int
+    d_qk: int = 576
+    sm_scale: float = 1.0 / math.sqrt(192.0)
+    invalid_frac: float = 0.0
+    empty_tokens: int = 0
+    seed: int = 0
+
+
+SPARSE_PREFILL = {
+    "dsv32_prefill": SparsePrefillSpec("dsv32_prefill", s_q=4096, num_heads=128, s_kv=32768,
+                                       topk=2048, seed=1101),
+}
+
+
+def make_sparse_prefill(spec: SparsePrefillSpec):
+    """(q bf16 [s_q, H, d_qk], kv bf16 [s_kv, d_qk], indices int32 [s_q, topk]) on the CPU."""
+    g = torch.Generator().manual_seed(spec.seed)
+    s_q, H, d, k, n = spec.s_q, spec.num_heads, spec.d_qk, spec.topk, spec.s_kv
+    q = torch.randn(s_q, H, d, generator=g).to(torch.bfloat16)
+    kv = torch.randn(n, d, generator=g).to(torch.bfloat16)
+    pos = torch.arange(s_q, dtype=torch.int64) + (n - s_q)
+    avail = (pos + 1).clamp(min=0)                           # rows of each token's prefix
+    ar = torch.arange(k, dtype=torch.int64)
+    # distinct rows: sorted draws from [0, avail - k] plus 0..k-1
+    span = (avail - k).clamp(min=0) + 1
+    draw = (torch.rand(s_q, k, generator=g, dtype=torch.float64) * span[:, None].double()).long()
+    draw = torch.sort(draw, dim=1).values + ar[None, :]
+    whole = torch.where(ar[None, :] < avail[:, None], ar[None, :], torch.full_like(draw, -1))
+    idx = torch.where((avail <= k)[:, None], whole, draw)
+    idx = idx[:, torch.randperm(k, generator=g)]
+    if spec.invalid_frac > 0:
+        hit = torch.rand(s_q, k, generator=g) < spec.invalid_frac
+        bad = torch.where(torch.rand(s_q, k, generator=g) < 0.5, torch.full_like(idx, -1),
+                          n + torch.randint(0, 1000, (s_q, k), generator=g))
+        idx = torch.where(hit, bad, idx)
+    if spec.empty_tokens > 0:
+        idx[:spec.empty_tokens] = -1
+    return q, kv, idx.to(torch.int32).contiguous()
