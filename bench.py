@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=None,
                     help="workload: 2 (default for decode), 1, 3 (default for kv_write), 4, 5, s1, s4")
-    ap.add_argument("--op", choices=("decode", "kv_write", "absorb", "swa_runs", "gather"), default="decode",
+    ap.add_argument("--op", choices=("decode", "kv_write", "absorb", "swa_runs", "gather",
+                                     "sparse_prefill"), default="decode",
                     help="decode: mla_decode + mla_combine (the default); kv_write: mla_kv_write "
                          "of every row of the workload's requests in one launch; absorb: "
                          "mla_q_absorb + mla_v_up for --tokens query tokens (DeepSeek-V3 dims)")
@@ -405,6 +406,87 @@ def bench_absorb(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_sparse_prefill(args):
+    """mla_sparse_prefill (metadata fill, plan, decode with per-row maxima, combine) on the
+    DeepSeek-V3.2-shaped prefill: 4096 tokens x 128 heads, 576-wide rows, top-k 2048 of a
+    32768-row buffer. One step = one call; the decode kernel takes nearly all of it."""
+    import torch
+    import mla_paged_latent_plan_amd as mla
+    from workloads import gen
+    spec = gen.SPARSE_PREFILL["dsv32_prefill"]
+    dev = torch.device("cuda:0")
+    q, kv, idx = gen.make_sparse_prefill(spec)
+    valid = int(((idx >= 0) & (idx < spec.s_kv)).sum())
+    qd, kvd, idd = q.to(dev), kv.to(dev), idx.to(dev)
+    cus = mla.device_num_cus()
+    H, s_q = spec.num_heads, spec.s_q
+    ws = torch.empty(mla.sparse_prefill_workspace_size(s_q, H, spec.d_qk, spec.topk, spec.s_kv, cus),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty(s_q, H, 512, dtype=torch.bfloat16, device=dev)
+    mlog = torch.empty(H, s_q, device=dev)
+    lse = torch.empty(H, s_q, device=dev)
+    stream = torch.cuda.current_stream()
+    sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sweep_out = torch.empty(1, dtype=torch.float32, device=dev)
+    call = lambda: mla.mla_sparse_prefill(qd, kvd, idd, spec.sm_scale, ws, out, mlog, lse, cus,
+                                          stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(ev(), ev()) for _ in range(K)]
+    for k in range(K):
+        if not args.no_flush:
+            torch.sum(sweep, dim=0, out=sweep_out[0])
+        a, e = evs[k]
+        a.record(stream)
+        call()
+        e.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(e) for a, e in evs])
+    t = float(ms.mean()) / 1e3
+    flops = 2.0 * valid * H * (spec.d_qk + 512)
+    nbytes = 2 * (q.numel() + kv.numel() + out.numel()) + 4 * (idx.numel() + 2 * H * s_q)
+    res = {
+        "metric": "MLA sparse prefill: query tokens/s, achieved MFMA TFLOP/s, % of roofline",
+        "value": round(s_q / t, 1), "unit": "query tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"sparse prefill {spec.name}: {s_q} tokens x {H} heads, d_qk "
+                               f"{spec.d_qk}, d_v 512, top-k {spec.topk} of {spec.s_kv} rows",
+                   "tokens": s_q, "parallelism": "single-gpu"},
+        "roofline": dict(bound="mfma", achieved=round(flops / t / 1e12, 2),
+                         peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
+                         frac=round(flops / t / 1e12 / MFMA_BF16_PEAK_TFS, 4), traffic=None,
+                         kernel="the whole call (metadata fill, plan, decode, combine)"),
+        "ms_p10_p90": [round(float(np.percentile(ms, 10)), 4),
+                       round(float(np.percentile(ms, 90)), 4)],
+        "algorithmic_flops": flops, "algorithmic_bytes": int(nbytes), "valid_entries": valid,
+        "cache_eviction": "none" if args.no_flush else "read-only 1 GiB sweep",
+    }
+    if not args.no_cpu:
+        from oracle.sparse_prefill import sparse_prefill
+        qn, kvn, ixn = q.float().numpy(), kv.float().numpy(), idx.numpy()
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < args.cpu_seconds and n < s_q:
+            sparse_prefill(qn, kvn, ixn, spec.sm_scale, tokens=[n])
+            n += 1
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = os.cpu_count() or 1
+        res["cpu_baseline"] = dict(value=round(n / dt, 2), unit="query tokens/s", cores=threads,
+                                   kind="oracle",
+                                   sample=f"the first {n} of {s_q} tokens, float64 numpy oracle "
+                                          f"(oracle/sparse_prefill.py), {dt:.1f} s")
+    print(json.dumps(res), flush=True)
+
+
 def bench_swa_runs(args):
     """mla_swa_runs over T tokens' 128-row windows (+ 3 drafts) in a ring of slots, pages of 64:
     the plan step of sliding-window layers, run once per forward."""
@@ -549,6 +631,8 @@ def main():
         return bench_absorb(args)
     if args.op == "swa_runs":
         return bench_swa_runs(args)
+    if args.op == "sparse_prefill":
+        return bench_sparse_prefill(args)
     if args.op == "gather":
         return bench_gather(args)
     import torch
