@@ -1,6 +1,5 @@
 """GPU parity of the sparse prefill (mla_sparse_prefill through the C ABI) against the oracle."""
 
-import dataclasses
 
 import numpy as np
 import pytest
@@ -97,3 +96,50 @@ def test_sparse_prefill_full_size_sampled():
     assert torch.isfinite(out.float()).all() and torch.isfinite(m).all() and torch.isfinite(l).all()
     gap = l - m  # 0 <= LSE - max <= ln(topk) (every list holds topk distinct valid rows)
     assert float(gap.min()) >= -LSE_ABS and float(gap.max()) <= np.log(spec.topk) + LSE_ABS
+
+
+def test_sparse_prefill_graph_replay_matches_eager():
+    """The whole call (metadata fill, plan, decode, combine) captured in a HIP graph: every replay
+    equals the eager result bitwise, with the outputs and the workspace overwritten by eager work
+    between replays (the call rebuilds its metadata and plan on every run)."""
+    spec = CASES[1]  # multi-split tokens: partials, split maxima and the combine
+    q, kv, idx = gen.make_sparse_prefill(spec)
+    cus = mla.device_num_cus()
+    qd, kvd, idd = q.cuda(), kv.cuda(), idx.cuda()
+    ws = torch.empty(mla.sparse_prefill_workspace_size(spec.s_q, spec.num_heads, spec.d_qk,
+                                                       spec.topk, spec.s_kv, cus),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty(spec.s_q, spec.num_heads, 512, dtype=torch.bfloat16, device="cuda")
+    mlog = torch.empty(spec.num_heads, spec.s_q, device="cuda")
+    lse = torch.empty(spec.num_heads, spec.s_q, device="cuda")
+    print("[sparse_prefill] graph replay: eager", flush=True)
+    mla.mla_sparse_prefill(qd, kvd, idd, spec.sm_scale, ws, out, mlog, lse, cus)
+    torch.cuda.synchronize()
+    ref = (out.clone(), mlog.clone(), lse.clone())
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        mla.mla_sparse_prefill(qd, kvd, idd, spec.sm_scale, ws, out, mlog, lse, cus, stream=cap)
+    torch.cuda.synchronize()
+    for k in range(4):
+        out.fill_(float("nan"))
+        mlog.fill_(0.0)
+        lse.fill_(0.0)
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        print(f"[sparse_prefill] graph replay {k}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), f"replay {k}: out"
+        assert torch.equal(mlog, ref[1]), f"replay {k}: max_logits"
+        assert torch.equal(lse, ref[2]), f"replay {k}: lse"
+
+
+def test_sparse_prefill_maximum_tokens():
+    """8192 tokens, the most one call takes (the plan's per-group state lives in LDS)."""
+    spec = S("max_tokens", s_q=8192, num_heads=16, s_kv=9000, topk=64, invalid_frac=0.1, seed=16)
+    print(f"[sparse_prefill] {spec}", flush=True)
+    inputs, out, mlog, lse = run(spec)
+    check(spec, out, mlog, lse, inputs, tokens=[0, 1, 63, 64, 4095, 8190, 8191])
+    assert torch.isfinite(out.float()).all()
