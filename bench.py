@@ -39,8 +39,8 @@ DECODE_SRC = os.path.join(ROOT, "mla_paged_latent_plan_amd", "csrc", "decode.hip
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=None,
                     help="workload: 2 (default for decode), 1, 3 (default for kv_write), 4, 5, s1, s4")
     ap.add_argument("--op", choices=("decode", "kv_write", "absorb", "swa_runs", "gather",
@@ -204,7 +204,20 @@ def cpu_baseline(wl, target_s):
     return dict(value=passes * n * s.q_len / dt, unit="query tokens/s", cores=int(threads),
                 kind="oracle",
                 sample=f"{passes} pass(es) over the first {n} of {s.batch} requests of the same "
-                       f"workload, float64 numpy oracle, {dt:.1f} s")
+                       f"workload, float64 numpy oracle, {dt:.1f} s",
+                os_cpu_count=os.cpu_count(), affinity=len(os.sched_getaffinity(0)),
+                cpu_model=cpu_model())
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_kv_write(kv_c, k_pe, fmt, target_s):
@@ -803,7 +816,11 @@ def main():
         "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
         "mfma_tflops": round(achieved_tfs, 2),
         "mfma_frac": round(achieved_tfs / MFMA_BF16_PEAK_TFS, 4),
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "ms_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)), 4),
+                                round(float(np.percentile(step_ms, 90)), 4)],
         "decode_ms": round(float(dec_ms.mean()), 4),
+        "decode_ms_median": round(float(np.median(dec_ms)), 4),
         "decode_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 4),
                               round(float(np.percentile(dec_ms, 90)), 4)],
         "combine_ms": round(float(com_ms.mean()), 4),
