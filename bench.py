@@ -63,6 +63,14 @@ def parse():
     return ap.parse_args()
 
 
+def emit(res):
+    """Print the JSON line; with a CPU baseline in the same unit, also the GPU/CPU speed ratio."""
+    cb = res.get("cpu_baseline")
+    if cb and cb.get("value") and cb.get("unit") == res.get("unit"):
+        res["gpu_cpu_speed_ratio"] = round(res["value"] / cb["value"], 1)
+    print(json.dumps(res), flush=True)
+
+
 def get_spec(name):
     from workloads import CONFIGS, SUPPLEMENTARY
     if name in SUPPLEMENTARY:
@@ -324,7 +332,7 @@ def bench_kv_write(args):
         res["cpu_baseline"] = cpu_kv_write(kv_c_h[:m].to(torch.float64).numpy(),
                                            k_pe_h[:m].to(torch.float64).numpy(), s.kv_format,
                                            args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    emit(res)
 
 
 def bench_absorb(args):
@@ -416,7 +424,7 @@ def bench_absorb(args):
                                    cores=threads, kind="oracle",
                                    sample=f"{n} pass(es) over all {T} tokens, float64 numpy oracle "
                                           f"(oracle/absorb.py), {dt:.1f} s")
-    print(json.dumps(res), flush=True)
+    emit(res)
 
 
 def bench_sparse_prefill(args):
@@ -497,7 +505,7 @@ def bench_sparse_prefill(args):
                                    kind="oracle",
                                    sample=f"the first {n} of {s_q} tokens, float64 numpy oracle "
                                           f"(oracle/sparse_prefill.py), {dt:.1f} s")
-    print(json.dumps(res), flush=True)
+    emit(res)
 
 
 def bench_swa_runs(args):
@@ -550,7 +558,7 @@ def bench_swa_runs(args):
         res["cpu_baseline"] = dict(value=round(n * T / dt, 1), unit="tokens/s", cores=1,
                                    kind="oracle", sample=f"{n} pass(es) over all {T} tokens, "
                                                          f"pure-Python oracle, {dt:.1f} s")
-    print(json.dumps(res), flush=True)
+    emit(res)
 
 
 def bench_gather(args):
@@ -629,7 +637,7 @@ def bench_gather(args):
         res["cpu_baseline"] = dict(value=round(passes * k / dt, 1), unit="rows/s", cores=1,
                                    kind="oracle", sample=f"{passes} pass(es) over the first {k} "
                                    f"output rows, float64 numpy oracle (oracle/gather.py), {dt:.1f} s")
-    print(json.dumps(res), flush=True)
+    emit(res)
 
 
 def main():
@@ -837,7 +845,7 @@ def main():
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    emit(res)
 
 
 if __name__ == "__main__":
