@@ -130,6 +130,7 @@ def algorithmic(wl):
 KERNEL_SOURCES = {
     "decode": ("decode.hip", "plan.hip", "mla_internal.h"),
     "kvwrite": ("kvwrite.hip", "mla_internal.h"),
+    "sparse_prefill": ("decode.hip", "plan.hip", "mla_internal.h"),
 }
 
 
@@ -466,6 +467,11 @@ def bench_sparse_prefill(args):
         e.record(stream)
     torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(e) for a, e in evs])
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     t = float(ms.mean()) / 1e3
     flops = 2.0 * valid * H * (spec.d_qk + 512)
     nbytes = 2 * (q.numel() + kv.numel() + out.numel()) + 4 * (idx.numel() + 2 * H * s_q)
@@ -480,8 +486,10 @@ def bench_sparse_prefill(args):
                    "tokens": s_q, "parallelism": "single-gpu"},
         "roofline": dict(bound="mfma", achieved=round(flops / t / 1e12, 2),
                          peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
-                         frac=round(flops / t / 1e12 / MFMA_BF16_PEAK_TFS, 4), traffic=None,
-                         kernel="the whole call (metadata fill, plan, decode, combine)"),
+                         frac=round(flops / t / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+                         traffic=measured_traffic("dsv32", kernel="sparse_prefill"),
+                         kernel="the whole call (metadata fill, plan, decode, combine); traffic: "
+                                "the decode kernel's"),
         "ms_p10_p90": [round(float(np.percentile(ms, 10)), 4),
                        round(float(np.percentile(ms, 90)), 4)],
         "algorithmic_flops": flops, "algorithmic_bytes": int(nbytes), "valid_entries": valid,
