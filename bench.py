@@ -668,6 +668,8 @@ def main():
     import mla_paged_latent_plan_amd as mla
     from workloads import make
 
+    from mla_paged_latent_plan_amd import _lib
+    build_id = _lib.check_build_id()
     spec = get_spec(args.config or "2")
     wl = make(spec)
     dev = torch.device("cuda:0")
@@ -847,9 +849,13 @@ def main():
         "wall_ms_per_step_with_flush": round(wall, 4),
         "cache_eviction": "none" if args.no_flush else
                           ("read-only 1 GiB sweep" if args.flush == "read" else "512 MB write fill"),
+        # the whole step (decode + combine) against the same roofline
+        "step_hbm_frac": round(alg["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_mfma_frac": round(alg["flops"] / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
         "algorithmic_bytes": alg["bytes"],
         "algorithmic_flops": alg["flops"],
         "source_hash": source_hash(),
+        "build_id": build_id,
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -190,10 +190,10 @@ int mla_q_absorb(int32_t tokens, int32_t num_heads, int32_t d_nope, int32_t d_la
 int mla_v_up(int32_t tokens, int32_t num_heads, int32_t d_latent, int32_t d_v, const void* o,
              const void* w_uv, void* out, void* stream);
 
-/* Run-compressed sliding windows (HALOps MLA API, mla_attention_plan: each token's SWA window is
- * compressed into at most two runs of consecutive slots; a run ends where the next slot is not the
- * previous one plus kv_run_step or lies on another page; a window of more than two runs, a padding
- * or not yet written window, is cut to its first row).
+/* Run-compressed sliding windows (HALOps MLA API, mla_attention_plan). With s_g the slot of window
+ * row g, rows g - 1 and g belong to one run iff s_g == s_{g-1} + kv_run_step and
+ * floor(s_g / page_size) == floor(s_{g-1} / page_size). A window is described by its runs when it
+ * has at most two; otherwise (a padding or not yet written window) only by its row 0.
  *   tokens        T >= 0 (0 enqueues nothing); topk >= 1 columns per window
  *   kv_indices    int32 [T, topk]: the cache slots of each token's window rows, in row order;
  *                 columns past the token's length are ignored
@@ -208,10 +208,11 @@ int mla_swa_runs(int32_t tokens, int32_t topk, const int32_t* kv_indices,
                  const int32_t* topk_lengths, int32_t page_size, int32_t kv_run_step, int32_t* runs,
                  void* stream);
 
-/* Chunked-context plan, on the host (vLLM mla_attention.py module docstring, the chunked prefill
- * approach: the context rows are gathered in chunks of at most W workspace rows; requests are packed
- * in order, the next request split on an aligned boundary when needed to fill W, so a chunk covers
- * a contiguous run of requests and no empty span). A chunk takes whole remainders of requests while
+/* Chunked-context plan, on the host: this library's own packing of the requests' context rows into
+ * chunks of at most W workspace rows (chunked context gathering is motivated by the vLLM
+ * mla_attention.py module docstring, the chunked prefill approach; the planner that page prints
+ * makes different plans and is not the one implemented here). Requests are packed in order, so a
+ * chunk covers a contiguous run of requests and no empty span. A chunk takes whole remainders of requests while
  * they fit; when the next does not, it takes that remainder's longest prefix that fits and whose
  * length is a multiple of `alignment`, then closes. Requests without context rows are in no chunk.
  *   num_reqs, context_lens (host int32 [num_reqs]; values < 0 count as 0)
@@ -279,6 +280,11 @@ int mla_sparse_prefill(int32_t s_q, int32_t num_heads, int32_t d_qk, int32_t top
 
 /* Static description of a status code. */
 const char* mla_strerror(int status);
+
+/* Static string identifying the sources the library was built from: 16 hex digits of the SHA-256
+ * of the HIP sources, internal headers and this header, computed by the build ("unknown" when
+ * built without it). A caller compares it with the same hash of the sources it expects. */
+const char* mla_build_id(void);
 
 #ifdef __cplusplus
 }

@@ -96,10 +96,16 @@ def mla_combine(p: Problem, num_cus: int, plan: torch.Tensor, partials: torch.Te
                 sink: Optional[torch.Tensor], out: torch.Tensor, lse: torch.Tensor,
                 stream=None) -> None:
     lib = _lib.load()
+    B, Sq, H = p.batch, p.q_len, p.num_heads
+    if tuple(out.shape) != (B, Sq, H, p.d_v):
+        raise ValueError(f"out must be [{B}, {Sq}, {H}, {p.d_v}], got {tuple(out.shape)}")
+    if lse.numel() != B * H * Sq:
+        raise ValueError(f"lse must hold [{B}, {H}, {Sq}], got {tuple(lse.shape)}")
     _lib.check("mla_combine", lib.mla_combine(
         p, num_cus, _ptr(plan, torch.uint8, "plan"), _ptr(partials, torch.uint8, "partials"),
         partials.numel(), _ptr(sink, torch.float32, "sink", p.num_heads),
-        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", B * H * Sq),
+        _stream(stream)))
 
 
 def mla_kv_write(p: Problem, kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor,

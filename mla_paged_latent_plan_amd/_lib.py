@@ -23,7 +23,8 @@ STATUS = {
 
 EXPORTS = ("mla_get_workspace_size", "mla_device_num_cus", "mla_decode_plan", "mla_decode",
            "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "mla_plan_context_chunks",
-           "mla_sparse_prefill_workspace_size", "mla_sparse_prefill", "mla_strerror")
+           "mla_sparse_prefill_workspace_size", "mla_sparse_prefill", "mla_build_id",
+           "mla_strerror")
 
 
 class MLAError(RuntimeError):
@@ -86,8 +87,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        vp, sz, vp, vp, vp, vp]
     lib.mla_strerror.argtypes = [ctypes.c_int]
     lib.mla_strerror.restype = ctypes.c_char_p
-    for name in EXPORTS[:-1]:
-        getattr(lib, name).restype = ctypes.c_int
+    lib.mla_build_id.argtypes = []
+    lib.mla_build_id.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        if name not in ("mla_strerror", "mla_build_id"):
+            getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -110,3 +114,18 @@ def device_num_cus() -> int:
     n = ctypes.c_int32(0)
     check("mla_device_num_cus", load().mla_device_num_cus(ctypes.byref(n)))
     return n.value
+
+
+def build_id() -> str:
+    """The source hash the loaded libmla.so was built from (mla_build_id)."""
+    return load().mla_build_id().decode()
+
+
+def check_build_id() -> str:
+    """Raise unless the loaded library was built from the sources in this tree; returns the id."""
+    from .build import source_id
+    got, want = build_id(), source_id()
+    if got != want:
+        raise ImportError(f"libmla.so was built from other sources (build id {got}, sources {want}): "
+                          "rebuild it with __graft_entry__.build()")
+    return got

@@ -2,6 +2,7 @@
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -11,6 +12,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
 SOURCES = ["plan.hip", "decode.hip", "combine.hip", "kvwrite.hip", "absorb.hip", "swa_runs.hip", "gather.hip", "sparse_meta.hip", "api.hip"]
+HEADERS = ["mla_internal.h", "layer_internal.h"]
+PUBLIC_HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "mla.h")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -30,11 +33,22 @@ def hipcc() -> str:
     return path
 
 
+def source_id() -> str:
+    """16 hex digits of the SHA-256 of every source the library is built from (the HIP sources,
+    internal headers and include/mla.h, in a fixed order). The build embeds it in libmla.so, where
+    mla_build_id() returns it, so a loaded library can be matched with the sources beside it."""
+    h = hashlib.sha256()
+    for path in [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [PUBLIC_HEADER]:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into libmla.so next to this file; returns the library path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *srcs, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, f'-DMLA_BUILD_ID="{source_id()}"', *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)

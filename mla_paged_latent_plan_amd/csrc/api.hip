@@ -6,6 +6,11 @@
 
 #include <math.h>
 
+// Hash of the sources the library was built from (set by the build; see mla_build_id).
+#ifndef MLA_BUILD_ID
+#define MLA_BUILD_ID "unknown"
+#endif
+
 using mla::PlanLayout;
 using mla::Shape;
 
@@ -221,6 +226,7 @@ int combine_impl(const mla_problem* p, int32_t num_cus, const void* plan, const 
   a.H = sh.H;
   a.R = sh.R;
   a.G = sh.G;
+  a.U = sh.U;
   a.sparse = sh.topk > 0;
   return launch_rc(mla::launch_combine(a, static_cast<hipStream_t>(stream)));
 }
@@ -516,6 +522,8 @@ int mla_plan_context_chunks(int32_t num_reqs, const int32_t* context_lens, int64
   *num_chunks = nc;
   return MLA_OK;
 }
+const char* mla_build_id(void) { return MLA_BUILD_ID; }
+
 const char* mla_strerror(int status) {
   switch (status) {
     case MLA_OK: return "ok";

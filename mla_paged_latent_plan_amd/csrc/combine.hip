@@ -41,6 +41,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int g = blockIdx.y;
+  if (!plan_matches(a.plan, a.G, a.U, a.R)) {
+    // a plan of another problem: the decode skipped its work, and every output row is NaN
+    const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (r >= a.R) return;
+    const int lane = threadIdx.x & 63;
+    const uint4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    *reinterpret_cast<uint4*>(a.out + ((int64_t)g * a.R + r) * kDv + 8 * lane) = nan4;
+    if (lane == 0) {
+      const int b = a.sparse ? g / a.Sq : g, t = a.sparse ? g % a.Sq : r / a.H, h = a.sparse ? r : r % a.H;
+      a.lse[((int64_t)b * a.H + h) * a.Sq + t] = __builtin_nanf("");
+      if (a.max_logits != nullptr) a.max_logits[((int64_t)b * a.H + h) * a.Sq + t] = __builtin_nanf("");
+    }
+    return;
+  }
   const int s0 = __builtin_amdgcn_readfirstlane(a.plan[a.grp_ptr_off + g]);
   const int s1 = __builtin_amdgcn_readfirstlane(a.plan[a.grp_ptr_off + g + 1]);
   const int ns = s1 - s0;

@@ -1317,7 +1317,7 @@ void decode_spec64_kernel(DecodeArgs a) {
   const lds_ptr base = (lds_ptr)lds;
   int unit, mt;
   unit_tile(blockIdx.x, a.m_tiles, &unit, &mt);
-  if (unit >= a.U) return;
+  if (unit >= a.U || !plan_matches(a.plan, a.G, a.U, a.R)) return;
   const int s0 = a.plan[a.unit_ptr_off + unit];
   const int s1 = a.plan[a.unit_ptr_off + unit + 1];
   Spec64<DQK, FP8> d(a, base);
@@ -1342,7 +1342,7 @@ void decode_kernel(DecodeArgs a) {
   const int m_tiles = a.m_tiles;
   const int unit = blockIdx.x / m_tiles;
   const int mt = blockIdx.x % m_tiles;
-  if (unit >= a.U) return;
+  if (unit >= a.U || !plan_matches(a.plan, a.G, a.U, a.R)) return;
   const int s0 = a.plan[a.unit_ptr_off + unit];
   const int s1 = a.plan[a.unit_ptr_off + unit + 1];
   Decoder<C> d(a, base);

@@ -93,9 +93,21 @@ struct CombineArgs {
   const float* part_max;  // with max_logits: per-split maxima written by the decode
   float* max_logits;      // optional, or nullptr
   int64_t grp_ptr_off;
-  int B, Sq, H, R, G;
+  int B, Sq, H, R, G, U;
   int sparse;
 };
+
+// Whether a plan's header describes the problem a kernel was launched for (magic word, groups,
+// units, stacked rows per group, partial slots): a plan built for another problem or CU count is
+// not used.
+__device__ __forceinline__ bool plan_matches(const int32_t* plan, int G, int U, int R) {
+  const int magic = __builtin_amdgcn_readfirstlane(plan[H_MAGIC]);
+  const int g = __builtin_amdgcn_readfirstlane(plan[H_G]);
+  const int u = __builtin_amdgcn_readfirstlane(plan[H_U]);
+  const int r = __builtin_amdgcn_readfirstlane(plan[H_R]);
+  const int smax = __builtin_amdgcn_readfirstlane(plan[H_SMAX]);
+  return magic == kPlanMagic && g == G && u == U && r == R && smax == G + U;
+}
 
 struct KvWriteArgs {
   const uint16_t* kv_c;  // bf16 [n][d_nope]

@@ -1,7 +1,7 @@
 // mla_swa_runs kernel: each token's sliding window of cache slots compressed into at most two runs
-// of consecutive slots (HALOps MLA API, mla_attention_plan). A run ends where the next row's slot is
-// not the previous slot plus kv_run_step or lies on another page; a window of more than two runs
-// (padding or not yet written) is cut to its first row. Output per token: (slot0, len0, slot1,
+// (HALOps MLA API, mla_attention_plan). With s_g the slot of row g, rows g - 1 and g share a run iff
+// s_g == s_{g-1} + kv_run_step and both lie on one page; a window with more than two runs (padding
+// or not yet written) is described by its row 0 alone. Output per token: (slot0, len0, slot1,
 // rows) — rows g < len0 at slot0 + step * g, the others at slot1 + step * (g - len0); slot1 = -1
 // without a second run; an empty window is (-1, 0, -1, 0).
 //

@@ -1,18 +1,18 @@
 """Chunked-context plan — oracle (test infrastructure), integer arithmetic only.
 
-vLLM mla_attention.py module docstring ("The chunked prefill approach"): the context rows the
-prefill must gather are bounded by a workspace of W rows; requests are packed in order, and the
-next request is split on an aligned boundary when needed to fill W, so a chunk covers a contiguous
-run of requests and no chunk holds an empty context span. (The gather kernel cannot start a split
-request off an alignment boundary, so a split request advances in aligned steps.)
+This is the library's own chunk planner, not the page's. The vLLM mla_attention.py module
+docstring ("The chunked prefill approach") only motivates it: the context rows a prefill gathers
+are bounded by a workspace of W rows, so they are gathered in chunks. The planner the page prints
+produces different plans (it has its own rules for empty contexts and for how much a split
+request takes) and is neither followed nor reproduced here.
 
-Reading of that description (the page's own planner is printed as a listing and is not followed):
+The library's rule:
 - Requests with no context rows belong to no chunk.
 - Walk the requests in order with a cursor (request r, first row s of what remains of it). A chunk
   takes whole remainders while they fit in W. When the next remainder does not fit, the chunk takes
   the longest prefix of it that fits and whose length is a multiple of the alignment A (a prefix of
   zero rows is not a span), then closes; the cursor moves past that prefix. A chunk is also closed
-  when it is full.
+  when it is full. (The gather starts a split request's next span on an alignment boundary.)
 - W must be at least A (else no row could ever be placed).
 
 The result is a list of chunks, each a list of spans (request, first row, rows).

@@ -1,11 +1,11 @@
 """Run-compressed sliding-window plan — oracle (test infrastructure), integer arithmetic only.
 
-HALOps MLA API, mla_attention_plan: each token's SWA window, given as the kv_cache slots of its
-rows (kv_indices [T, topk], the first topk_lengths[t] columns valid), is described by at most two
-runs of consecutive slots. A run ends where the next row's slot is not the previous slot plus
-kv_run_step (1 or -1) or lies on another page (page = slot // page_size). A window of more than
-two runs (a padding or not yet written window) is cut to its first row. The result per token is
-(slot0, len0, slot1, rows): rows is the effective length, the first len0 rows form the first run.
+HALOps MLA API, mla_attention_plan. A token's SWA window is given as the cache slots s_0, s_1, ...
+of its rows (kv_indices [T, topk], the first topk_lengths[t] columns valid). Rows g - 1 and g are
+in one run iff s_g == s_{g-1} + kv_run_step (1 or -1) and s_g // page_size == s_{g-1} // page_size.
+A window with at most two runs is described by them; one with more (a padding or not yet written
+window) is described by its row 0 alone. The result per token is (slot0, len0, slot1, rows): rows is
+the effective length, the first len0 rows form the first run.
 
 Readings where the page leaves a point open:
 - Row g of a run starting at slot s sits at s + kv_run_step * g (the page writes slot0 + g, which

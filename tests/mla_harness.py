@@ -152,9 +152,27 @@ def metrics(out: torch.Tensor, lse: torch.Tensor, O_ref: np.ndarray, L_ref: np.n
     )
 
 
-def assert_parity(m: dict, rel_l2=REL_L2, max_abs=MAX_ABS, lse_abs=LSE_ABS, ctx=""):
+def scaled_bound(wl) -> bool:
+    """Whether the max-abs bar of a workload is taken relative to the term magnitudes.
+
+    Only fp8 rows whose ue8m0 scale exponents are not all zero: their terms reach 2^4 x 448 and the
+    bf16 rounding of the probabilities then leaves an error proportional to those terms (terms of
+    size 30 that cancel to |O| = 1 keep an error of order 0.06). Every other case, bf16 rows and
+    fp8 rows at exponent 0, is held to the plain bound |O - O_ref| <= 2e-2."""
+    s = wl.spec
+    return s.kv_format == "fp8" and tuple(s.scale_exp_range) != (0, 0)
+
+
+def assert_parity(m: dict, rel_l2=REL_L2, max_abs=MAX_ABS, lse_abs=LSE_ABS, ctx="",
+                  scaled: bool = False):
+    """The parity bar: rel-L2, LSE and, per element, the plain max-abs bound (or, with scaled, the
+    bound relative to max(1, sum_j P_j |V_j|)); the message carries both max-abs figures."""
+    nums = f"max_abs={m['max_abs']:.3e} max_abs_scaled={m['max_abs_scaled']:.3e}"
     assert m["finite"], f"{ctx} non-finite outputs {m}"
     assert m["lse_inf_ok"], f"{ctx} empty rows must give LSE -inf {m}"
     assert m["rel_l2"] <= rel_l2, f"{ctx} rel-L2 {m}"
-    assert m["max_abs_scaled"] <= max_abs, f"{ctx} max-abs {m}"
+    if scaled:
+        assert m["max_abs_scaled"] <= max_abs, f"{ctx} scaled max-abs ({nums}) {m}"
+    else:
+        assert m["max_abs"] <= max_abs, f"{ctx} max-abs ({nums}) {m}"
     assert m["lse_max_abs"] <= lse_abs, f"{ctx} LSE {m}"

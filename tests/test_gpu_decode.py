@@ -93,7 +93,7 @@ def test_parity(name, cus):
     O, L, A = H.oracle_of(wl, abs_mass=True)
     m = H.metrics(out, lse, O, L, A)
     print(f"[gpu]   {m}", flush=True)
-    H.assert_parity(m, ctx=f"{name}/{cus}")
+    H.assert_parity(m, ctx=f"{name}/{cus}", scaled=H.scaled_bound(wl))
     want = H.plan_words(wl, used)
     got = plan.view(torch.int32).numpy()[:len(want)]
     assert np.array_equal(got, want), f"plan differs for {name}/{cus}"
@@ -146,7 +146,7 @@ def test_fp8_extreme_scales_uniform_scores():
     O, L, A = H.oracle_of(wl, abs_mass=True)
     m = H.metrics(out, lse, O, L, A)
     print(f"[gpu]   {m}", flush=True)
-    H.assert_parity(m, ctx="fp8 extreme scales")
+    H.assert_parity(m, ctx="fp8 extreme scales", scaled=H.scaled_bound(wl))
     for b in range(2):
         np.testing.assert_allclose(lse[b, :, 0].numpy(), math.log(int(wl.seqlens[b])), atol=1e-4)
 
@@ -166,16 +166,24 @@ def test_sparse_arange_equals_dense():
     assert m["max_abs"] <= 1e-2 and m["lse_max_abs"] <= 1e-4, m
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5, "s1", "s4"])
+FULL_SIZE = {2: CONFIGS[2], 3: CONFIGS[3], 4: CONFIGS[4], 5: CONFIGS[5],
+             "s1": SUPPLEMENTARY["s1"], "s4": SUPPLEMENTARY["s4"],
+             # config 3 with every scale exponent 0: held to the plain max-abs bound
+             "3_exp0": dataclasses.replace(CONFIGS[3], name="dsv3_fp8_exp0", scale_exp_range=(0, 0))}
+
+
+@pytest.mark.parametrize("cfg", list(FULL_SIZE))
 def test_full_size_configs(cfg):
     """The benchmark workloads at their full sizes, in the launch configuration the bench uses."""
-    wl = make(SUPPLEMENTARY[cfg] if isinstance(cfg, str) else CONFIGS[cfg])
+    wl = make(FULL_SIZE[cfg])
     print(f"[gpu] full-size config {cfg}", flush=True)
     out, lse, plan, used = H.run_gpu(wl)
     O, L, A = H.oracle_of(wl, abs_mass=True)
     m = H.metrics(out, lse, O, L, A)
-    print(f"[gpu]   {m}", flush=True)
-    H.assert_parity(m, ctx=f"config {cfg}")
+    print(f"[gpu]   config {cfg}: max_abs={m['max_abs']:.4e} max_abs_scaled={m['max_abs_scaled']:.4e} "
+          f"rel_l2={m['rel_l2']:.4e} lse={m['lse_max_abs']:.3e} (bound: "
+          f"{'scaled' if H.scaled_bound(wl) else 'plain'})", flush=True)
+    H.assert_parity(m, ctx=f"config {cfg}", scaled=H.scaled_bound(wl))
     want = H.plan_words(wl, used)
     assert np.array_equal(plan.view(torch.int32).numpy()[:len(want)], want)
 
@@ -239,7 +247,7 @@ def test_maximum_sizes(case):
     O, L, A = H.oracle_of(wl, abs_mass=True)
     m = H.metrics(out, lse, O, L, A)
     print(f"[gpu]   {m}", flush=True)
-    H.assert_parity(m, ctx=case)
+    H.assert_parity(m, ctx=case, scaled=H.scaled_bound(wl))
     want = H.plan_words(wl, used)
     assert np.array_equal(plan.view(torch.int32).numpy()[:len(want)], want)
 
@@ -259,7 +267,7 @@ def test_sparse_duplicate_indices_count_per_occurrence():
     O, L, A = H.oracle_of(wl, abs_mass=True)
     m = H.metrics(out, lse, O, L, A)
     print(f"[gpu]   {m}", flush=True)
-    H.assert_parity(m, ctx="duplicate indices")
+    H.assert_parity(m, ctx="duplicate indices", scaled=H.scaled_bound(wl))
     half = dataclasses.replace(spec, topk=64, name="dup_idx_half")
     wl2 = make(half)
     wl2.indices = torch.from_numpy(np.ascontiguousarray(idx[:, :, :64]))
@@ -267,3 +275,53 @@ def test_sparse_duplicate_indices_count_per_occurrence():
     np.testing.assert_allclose(lse.numpy(), lse2.numpy() + math.log(2.0), atol=1e-4)
     np.testing.assert_allclose(out.to(torch.float64).numpy(), out2.to(torch.float64).numpy(),
                                atol=2e-2)
+
+
+@pytest.mark.parametrize("case", ["h16_bf16", "h128_fp8"])
+def test_combine_past_64_splits(case):
+    """One long request spread over the device's CUs: its group has more than 64 splits, so the
+    combine walks its split LSEs and partial rows in several 64-split chunks."""
+    if case == "h16_bf16":
+        spec = Spec("long_h16", batch=2, q_len=1, num_heads=16, page_size=64,
+                    seqlens=(131072, 100), sm_scale=S, seed=81)
+    else:
+        spec = Spec("long_h128_fp8", batch=2, q_len=1, num_heads=128, page_size=64,
+                    kv_format="fp8", seqlens=(131072, 100), sm_scale=S, seed=82)
+    wl = make(spec)
+    print(f"[gpu] combine past 64 splits: {case}", flush=True)
+    out, lse, plan, used = H.run_gpu(wl)
+    want = H.plan_words(wl, used)
+    words = plan.view(torch.int32).numpy()[:len(want)]
+    assert np.array_equal(words, want)
+    grp_ptr = words[16:16 + spec.batch + 1]
+    nsplit = np.diff(grp_ptr)
+    print(f"[gpu]   splits per group {nsplit.tolist()} on {used} CUs", flush=True)
+    assert nsplit[0] > 64, f"the long request has only {nsplit[0]} splits"
+    O, L, A = H.oracle_of(wl, abs_mass=True)
+    m = H.metrics(out, lse, O, L, A)
+    print(f"[gpu]   {m}", flush=True)
+    H.assert_parity(m, ctx=case, scaled=H.scaled_bound(wl))
+
+
+def test_plan_of_other_cu_count_gives_nan():
+    """A plan built for another CU count (other units, other split records) is not used: the
+    decode skips its work and the combine writes NaN to every output row and LSE."""
+    import mla_paged_latent_plan_amd as mla
+    wl = _make("h128_edges")
+    dev = H.to_device(wl)
+    p = H.problem_of(wl, mla)
+    s = wl.spec
+    cus = mla.device_num_cus()
+    plan_bytes, part_bytes = mla.workspace_size(p, cus)
+    plan_small, _ = mla.workspace_size(p, 1)
+    plan = torch.zeros(max(plan_bytes, plan_small), dtype=torch.uint8, device="cuda")
+    partials = torch.zeros(part_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(s.batch, s.q_len, s.num_heads, s.d_v, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(s.batch, s.num_heads, s.q_len, dtype=torch.float32, device="cuda")
+    print("[gpu] plan of another CU count", flush=True)
+    mla.mla_decode_plan(p, 1, dev.seqlens, None, plan)  # planned for one CU
+    mla.mla_decode(p, cus, dev.q, dev.cache, dev.block_table, dev.seqlens, s.sm_scale, None, None,
+                   plan, partials, out, lse)
+    mla.mla_combine(p, cus, plan, partials, None, out, lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all() and torch.isnan(lse).all()
