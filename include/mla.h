@@ -71,7 +71,8 @@ typedef enum mla_status {
   MLA_ERR_WORKSPACE = 6,  /* plan or partial buffer smaller than mla_get_workspace_size says  */
   MLA_ERR_ALIGN = 7,      /* a pointer is not 16-byte aligned                                */
   MLA_ERR_DEVICE = 8,     /* HIP device query failed                                         */
-  MLA_ERR_LAUNCH = 9      /* a kernel launch failed                                          */
+  MLA_ERR_LAUNCH = 9,     /* a kernel launch failed                                          */
+  MLA_ERR_SCRATCH = 10    /* mla_decode_noalloc: plan + partials exceed the static scratch   */
 } mla_status;
 
 typedef enum mla_kv_format {
@@ -146,6 +147,24 @@ int mla_decode(const mla_problem* p, int32_t num_cus, const void* q, const void*
  * then the sink; a group with no rows gets O = 0 and LSE = -inf (or LSE = sink_h). */
 int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const void* partials,
                 size_t partial_bytes, const float* sink, void* out, float* lse, void* stream);
+
+/* Allocation-free decode step, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): mla_decode_plan,
+ * mla_decode and mla_combine enqueued in one call, with the plan and the split partials held in
+ * the library's own static device scratch of 64 MiB per GPU (allocated with the library's code
+ * object on each device it runs on, kept until the process ends) instead of caller buffers. The
+ * arguments are those of the three calls it stands for (topk_lens as in mla_decode_plan); the
+ * outputs equal theirs bit for bit. A problem whose plan (rounded up to 256 bytes) plus partial
+ * bytes (mla_get_workspace_size) exceed 64 MiB is rejected with MLA_ERR_SCRATCH before anything is
+ * enqueued. The call allocates and frees nothing. Every call on one GPU uses that GPU's one
+ * scratch and the plan kernel rewrites all of it that the decode and combine read, so nothing has
+ * to be cleared between calls; but calls whose work overlaps on one GPU (other streams, other
+ * threads, or an earlier call's graph replay still running) race on the scratch and must be
+ * ordered by the caller. */
+int mla_decode_noalloc(const mla_problem* p, int32_t num_cus, const void* q, const void* kv_cache,
+                       const int32_t* block_table, const int32_t* seqlens,
+                       const int32_t* topk_lens, float sm_scale, const int32_t* indices,
+                       const float* sink, void* out, float* lse, void* stream);
 
 /* Cache write (vLLM mla_attention.py update_kv_cache(kv_c_normed, k_pe, kv_cache, slot_mapping,
  * ...); HALOps MLA API, mla_attention kv_cache: each token's new row is written in place).

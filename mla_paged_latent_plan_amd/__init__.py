@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import MLA_KV_BF16, MLA_KV_FP8, MLAError, Problem  # noqa: F401
 
 __all__ = ["Problem", "make_problem", "workspace_size", "mla_decode_plan", "mla_decode",
-           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "plan_context_chunks",
+           "mla_combine", "mla_decode_noalloc", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "plan_context_chunks",
            "sparse_prefill_workspace_size", "mla_sparse_prefill", "MLADecode", "device_num_cus",
            "MLAError"]
 
@@ -104,6 +104,34 @@ def mla_combine(p: Problem, num_cus: int, plan: torch.Tensor, partials: torch.Te
     _lib.check("mla_combine", lib.mla_combine(
         p, num_cus, _ptr(plan, torch.uint8, "plan"), _ptr(partials, torch.uint8, "partials"),
         partials.numel(), _ptr(sink, torch.float32, "sink", p.num_heads),
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", B * H * Sq),
+        _stream(stream)))
+
+
+def mla_decode_noalloc(p: Problem, num_cus: int, q: torch.Tensor, kv_cache: torch.Tensor,
+                       block_table: torch.Tensor, seqlens: torch.Tensor,
+                       topk_lens: Optional[torch.Tensor], sm_scale: float,
+                       indices: Optional[torch.Tensor], sink: Optional[torch.Tensor],
+                       out: torch.Tensor, lse: torch.Tensor, stream=None) -> None:
+    """plan + decode + combine with the plan and partials in the library's static device scratch
+    (no buffer of the caller's beyond inputs and outputs)."""
+    lib = _lib.load()
+    B, Sq, H = p.batch, p.q_len, p.num_heads
+    if tuple(q.shape) != (B, Sq, H, p.d_qk):
+        raise ValueError(f"q must be [{B}, {Sq}, {H}, {p.d_qk}], got {tuple(q.shape)}")
+    if tuple(out.shape) != (B, Sq, H, p.d_v):
+        raise ValueError(f"out must be [{B}, {Sq}, {H}, {p.d_v}], got {tuple(out.shape)}")
+    if kv_cache.numel() < p.num_pages * p.page_stride_bytes // kv_cache.element_size():
+        raise ValueError("kv_cache is smaller than num_pages * page_stride_bytes")
+    if tuple(block_table.shape) != (B, p.max_pages_per_seq):
+        raise ValueError("block_table must be [batch, max_pages_per_seq]")
+    if p.topk > 0 and (indices is None or tuple(indices.shape) != (B, Sq, p.topk)):
+        raise ValueError("indices must be [batch, q_len, topk] when topk > 0")
+    _lib.check("mla_decode_noalloc", lib.mla_decode_noalloc(
+        p, num_cus, _ptr(q, torch.bfloat16, "q"), kv_cache.data_ptr(),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(seqlens, torch.int32, "seqlens", B),
+        _ptr(topk_lens, torch.int32, "topk_lens", B * Sq), float(sm_scale),
+        _ptr(indices, torch.int32, "indices"), _ptr(sink, torch.float32, "sink", H),
         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", B * H * Sq),
         _stream(stream)))
 

@@ -18,11 +18,11 @@ MLA_KV_FP8 = 1
 STATUS = {
     0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_FORMAT", 4: "MLA_ERR_PAGE",
     5: "MLA_ERR_MODE", 6: "MLA_ERR_WORKSPACE", 7: "MLA_ERR_ALIGN", 8: "MLA_ERR_DEVICE",
-    9: "MLA_ERR_LAUNCH",
+    9: "MLA_ERR_LAUNCH", 10: "MLA_ERR_SCRATCH",
 }
 
 EXPORTS = ("mla_get_workspace_size", "mla_device_num_cus", "mla_decode_plan", "mla_decode",
-           "mla_combine", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "mla_plan_context_chunks",
+           "mla_combine", "mla_decode_noalloc", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "mla_plan_context_chunks",
            "mla_sparse_prefill_workspace_size", "mla_sparse_prefill", "mla_build_id",
            "mla_strerror")
 
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode.argtypes = [P, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp, vp,
                                vp]
     lib.mla_combine.argtypes = [P, i32, vp, vp, sz, vp, vp, vp, vp]
+    lib.mla_decode_noalloc.argtypes = [P, i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
+                                       vp]
     lib.mla_kv_write.argtypes = [P, ctypes.c_int64, vp, vp, vp, vp, vp]
     lib.mla_q_absorb.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.mla_v_up.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]

@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 // Hash of the sources the library was built from (set by the build; see mla_build_id).
 #ifndef MLA_BUILD_ID
 #define MLA_BUILD_ID "unknown"
@@ -292,6 +294,74 @@ int mla_combine(const mla_problem* p, int32_t num_cus, const void* plan, const v
                       stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Device scratch of mla_decode_noalloc: the plan, then the split partials, of the last call on each
+// device. A file-scope device array exists once per GPU the library runs on and lives until the
+// process ends. In host code `scratch` names a host-side stand-in, so its device address is taken
+// once per device with hipGetSymbolAddress and only that address is used.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch (resolved on the first call on that device).
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return MLA_ERR_DEVICE;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_noalloc(const mla_problem* p, int32_t num_cus, const void* q, const void* kv_cache,
+                       const int32_t* block_table, const int32_t* seqlens,
+                       const int32_t* topk_lens, float sm_scale, const int32_t* indices,
+                       const float* sink, void* out, float* lse, void* stream) {
+  Shape sh;
+  int rc = derive(p, num_cus, &sh);
+  if (rc != MLA_OK) return rc;
+  if (num_cus <= 0) {
+    rc = query_cus(&num_cus);
+    if (rc != MLA_OK) return rc;
+  }
+  const size_t plan_bytes = round256((size_t)PlanLayout::make(sh.G, sh.U).bytes);
+  const size_t part_bytes = partial_size(sh);
+  if (plan_bytes + part_bytes > kScratchBytes) return MLA_ERR_SCRATCH;
+  // the same host checks as the calls it stands for, before anything is enqueued
+  if (q == nullptr || kv_cache == nullptr || block_table == nullptr || seqlens == nullptr ||
+      out == nullptr || lse == nullptr || (sh.topk > 0 && indices == nullptr))
+    return MLA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out)) return MLA_ERR_ALIGN;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return MLA_ERR_SHAPE;
+  void* base = nullptr;
+  rc = scratch_address(&base);
+  if (rc != MLA_OK) return rc;
+  uint8_t* plan = static_cast<uint8_t*>(base);
+  uint8_t* partials = plan + plan_bytes;
+  rc = mla_decode_plan(p, num_cus, seqlens, topk_lens, plan, plan_bytes, stream);
+  if (rc != MLA_OK) return rc;
+  rc = decode_impl(p, num_cus, q, kv_cache, block_table, seqlens, sm_scale, indices, sink, plan,
+                   partials, part_bytes, out, lse, nullptr, nullptr, stream);
+  if (rc != MLA_OK) return rc;
+  return combine_impl(p, num_cus, plan, partials, part_bytes, sink, out, lse, nullptr, nullptr,
+                      stream);
+}
+
 int mla_sparse_prefill_workspace_size(int32_t s_q, int32_t num_heads, int32_t d_qk, int32_t topk,
                                       int64_t s_kv, int32_t num_cus, size_t* workspace_bytes) {
   SparseLayout L;
@@ -536,6 +606,7 @@ const char* mla_strerror(int status) {
     case MLA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case MLA_ERR_DEVICE: return "HIP device query failed";
     case MLA_ERR_LAUNCH: return "kernel launch failed";
+    case MLA_ERR_SCRATCH: return "plan and partials exceed the library's static device scratch";
     default: return "unknown status";
   }
 }

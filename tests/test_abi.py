@@ -233,3 +233,19 @@ def test_sparse_prefill_host_checks(lib):
     assert call(a7=vp(4100)) == 7 and call(a12=vp(4104)) == 7
     assert call(a9=0.0) == 2 and call(a9=float("nan")) == 2
     assert call(a11=16) == 6
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    """mla_decode_noalloc: a problem whose plan and partials exceed the static scratch (512
+    requests of 4 tokens x 64 heads on 256 CUs: about 151 MB of partials) is refused before
+    anything is enqueued; NULL inputs are refused too."""
+    p = good(batch=512, q_len=4, num_heads=64, d_qk=512, page_size=64, page_stride_bytes=64 * 1024,
+             num_pages=10, max_pages_per_seq=8, causal=1, window=128)
+    nz = ctypes.c_void_p(16)
+    rc = lib.mla_decode_noalloc(ctypes.byref(p), 256, nz, nz, nz, nz, None, 0.1, None, None, nz,
+                                nz, None)
+    assert rc == 10 and lib.mla_strerror(rc).decode().startswith("plan and partials exceed")
+    small = good()
+    rc = lib.mla_decode_noalloc(ctypes.byref(small), 256, None, nz, nz, nz, None, 0.1, None, None,
+                                nz, nz, None)
+    assert rc == 1
