@@ -771,12 +771,13 @@ __device__ __forceinline__ void mfma_sq2_cvt_last(f32x4& c0, f32x4& c1, const bf
       : "+v"(c0), "+v"(c1)
       : "v"(a0), "v"(a1), "a"(b));
 }
-template <int N>
-__device__ __forceinline__ void mfma_drain_acc(f32x4 (&o)[N][4]) {
+template <int N, int M>
+__device__ __forceinline__ void mfma_drain_acc(f32x4 (&o)[N][M]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" ::: "memory");
 #pragma unroll
   for (int i = 0; i < N; ++i)
-    asm volatile("" : "+a"(o[i][0]), "+a"(o[i][1]), "+a"(o[i][2]), "+a"(o[i][3]));
+#pragma unroll
+    for (int k = 0; k < M; ++k) asm volatile("" : "+a"(o[i][k]));
 }
 
 // 64 query rows per workgroup, eight waves in two roles, two waves per SIMD:
@@ -1008,7 +1009,7 @@ struct Spec64 {
           }
           return raw;
         };
-        constexpr int D = 4;  // operand steps in flight
+        constexpr int D = 2;  // operand steps in flight
         bf16x8 ka[D][2];
 #pragma unroll
         for (int i = 0; i < D - 1; ++i)
@@ -1302,6 +1303,671 @@ struct Spec64 {
   }
 };
 
+// VGPR-only MFMA forms for the 128-row kernel. A kernel that holds anything in accumulation
+// registers gets its 256 registers per wave split evenly between the two files; this one needs
+// about 200 registers of long-lived accumulators and operands and 50 of temporaries, so it keeps
+// everything in the 256 architectural VGPRs (MFMAs read and write them directly).
+__device__ __forceinline__ void mfma_vv(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vv0(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+template <int N, int M>
+__device__ __forceinline__ void mfma_drain_v(f32x4 (&o)[N][M]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int k = 0; k < M; ++k) asm volatile("" : "+v"(o[i][k]));
+}
+
+// 128 query rows per workgroup (all heads of a DeepSeek-V3 request, so every KV row is taken in by
+// one CU only), eight waves in two roles, two waves per SIMD:
+//  * score wave s (waves 0-3): QK^T and the softmax of query rows [32s, 32s + 32) of the tile (the
+//    latent part of Q^T held in registers, its RoPE part in LDS), and PV of those rows for output
+//    columns [128s, 128s + 128), one step behind like the value waves;
+//  * value wave s (waves 4-7, on the SIMD of score wave s): PV of the other 96 rows for output
+//    columns [128s, 128s + 128), one step behind the score waves, plus every global -> LDS
+//    transfer (rows with the streaming cache policy: each row is read once).
+// MAXL: also track each row's true maximum score (the max_logits output).
+// Inside a split the two roles are ordered by counters in LDS, not workgroup barriers, so the score
+// waves can run QK^T of step t + 1 while the value waves accumulate step t:
+//  * LANDED: a value wave signals when its rows of a step have arrived; the score waves start step
+//    t once all four have (for step t);
+//  * PREADY / PCONSUMED: the score waves publish P^T of step t (double-buffered, with its rescale
+//    factors and flags) and signal; the value waves take it into registers and signal; P^T of
+//    step t + 2 overwrites the buffer only after that;
+//  * RELEASED: every wave signals when it has read the rows of step t for the last time; then the
+//    value waves send the rows of step t + 3 into that slot (three slots, so steps t + 1 and t + 2
+//    are landing meanwhile).
+// A wait only ever depends on signals of earlier steps or of the other role's same step that come
+// before its own waits, so no cycle can form.
+template <int DQK, bool MAXL>
+struct Spec128 {
+  static constexpr bool HAS_B = DQK > 512;                 // RoPE region present
+  static constexpr int KS = DQK / 32;                      // 32-wide k steps of QK^T
+  static constexpr int KSQ = 16;                           // k steps of Q^T held in registers
+  static constexpr int kRows = 32;                         // rows per slot / step
+  static constexpr int kSlotA = kRows * kRowStrideA;
+  static constexpr int kSlot = kSlotA + (HAS_B ? kRows * 128 : 0);
+  static_assert(kSlot % 256 == 0, "slot bases keep the low byte of in-slot offsets");
+  static constexpr uint32_t kPOff = 3 * kSlot;             // P^T [2 steps][8 row tiles][64 lanes] x 16 B
+  static constexpr uint32_t kQrOff = kPOff + 2 * 8192;     // Q RoPE part [128 rows][128 B], swizzled
+  static constexpr int kStageRow = 1040;                   // output staging rows (epilogue)
+  static constexpr uint32_t kStatOff =                     // above the Q RoPE part and the staging
+      (kQrOff + (HAS_B ? 128 * 128 : 0)) > 128 * kStageRow ? kQrOff + (HAS_B ? 128 * 128 : 0)
+                                                            : 128 * kStageRow;
+  static constexpr uint32_t kAOff = kStatOff;              // rescale factors [2 steps][128]
+  static constexpr uint32_t kFOff = kAOff + 1024;          // rescale flags [2 steps][4]
+  static constexpr uint32_t kCOff = kFOff + 32;            // step counters, one per signalling wave:
+  static constexpr uint32_t kCLanded = kCOff;              //   [4] bundles landed, per value wave
+  static constexpr uint32_t kCPReady = kCOff + 16;         //   [4] P^T published, per score wave
+  static constexpr uint32_t kCPConsumed = kCOff + 32;      //   [4] P^T taken into registers, per value wave
+  static constexpr uint32_t kCReleased = kCOff + 48;       //   [8] steps whose rows a wave has finished
+  static constexpr uint32_t kMOff = kCOff + 80;            // row-valid masks [4 steps][4 bytes]
+  static constexpr uint32_t kLOff = kMOff + 16;            // final l [128], then m [128]
+  static constexpr uint32_t kRiOff = kLOff + 1024;         // per value wave: block-table entries
+  static constexpr int kRiWave = 4 * 32 + 8 * 32;          //   [4][8], index entries [8][8]
+  static constexpr int LDS = kRiOff + 4 * kRiWave;
+  static_assert(LDS <= 160 * 1024, "LDS of one workgroup");
+  static_assert(128 * kStageRow <= kStatOff, "output staging fits below the row statistics");
+  static constexpr int kDmaOps = 8 + (HAS_B ? 1 : 0);      // row LDS-DMA instructions per bundle
+
+  const DecodeArgs& a;
+  lds_ptr sm;
+  int lane, wave;
+  int g, b, L, j0, n, q0, qend, nsplit, cur_split;
+
+  __device__ Spec128(const DecodeArgs& args, lds_ptr base) : a(args), sm(base) {
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  }
+
+  __device__ __forceinline__ static uint32_t slot_of(int x) { return (uint32_t)(x % 3) * kSlot; }
+  // The lane index as a value the compiler cannot treat as loop-invariant: addresses derived from
+  // it are recomputed in each step (a few VALU instructions) instead of being hoisted and held in
+  // registers across the whole split.
+  __device__ __forceinline__ int opaque_lane() const {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  }
+  // Step counters in LDS replace workgroup barriers inside a split. Each signalling wave owns one
+  // counter, the number of steps it has completed for that purpose, and writes it (one lane); a
+  // waiting wave polls until the smallest of the counters it depends on has reached a step. The LDS
+  // executes one wave's instructions in issue order, so a counter write cannot overtake the wave's
+  // earlier LDS reads or writes it vouches for; transfers by LDS-DMA are covered by the issuing
+  // wave's vmcnt wait before it signals. (One shared counter would not do: the waves of a role drift
+  // apart by up to a step, and a count could then be reached with one wave's later signal standing
+  // in for another wave's missing earlier one.) Counters are cleared in the split's prologue.
+  __device__ __forceinline__ void signal(uint32_t ctr, int idx, int count) const {
+    asm volatile("" ::: "memory");  // after every LDS access above, in program order
+    if (lane == 0) *reinterpret_cast<volatile LDS_AS int*>(sm + ctr + 4 * idx) = count;
+    asm volatile("" ::: "memory");
+  }
+  // Polled by lane 0 alone (16 bytes per poll, not 1 KB).
+  __device__ __forceinline__ int min4(uint32_t ctr) const {
+    int m = 0;
+    if (lane == 0) {
+      const u32x4 c = *reinterpret_cast<volatile LDS_AS u32x4*>(sm + ctr);
+      m = min(min((int)c[0], (int)c[1]), min((int)c[2], (int)c[3]));
+    }
+    return __builtin_amdgcn_readfirstlane(m);
+  }
+  __device__ __forceinline__ void wait4(uint32_t ctr, int target) const {
+    while (min4(ctr) < target) __builtin_amdgcn_s_sleep(1);
+  }
+  __device__ __forceinline__ void wait8(uint32_t ctr, int target) const {
+    while (min(min4(ctr), min4(ctr + 16)) < target) __builtin_amdgcn_s_sleep(1);
+  }
+
+  // ===== value waves: row description pipeline and DMA =======================================
+  __device__ __forceinline__ int vrow() const { return 8 * (wave - 4) + (lane & 7); }
+  __device__ __forceinline__ uint32_t pg_slot(int x) const {
+    return kRiOff + (wave - 4) * kRiWave + (x & 3) * 32;
+  }
+  __device__ __forceinline__ uint32_t ix_slot(int x) const {
+    return kRiOff + (wave - 4) * kRiWave + 128 + (x & 7) * 32;
+  }
+  __device__ __forceinline__ void dma_dword(const int32_t* src, uint32_t dst) const {
+    if (lane < 8) dma_x1(src, lds_addr(sm + dst));
+  }
+  __device__ __forceinline__ int ri_read(uint32_t slot) const {
+    return *reinterpret_cast<const LDS_AS int*>(sm + slot + 4 * (lane & 7));
+  }
+  __device__ __forceinline__ void idx_fetch(int x) const {  // index entries of step x
+    const int k = min(32 * x + vrow(), a.topk - 1);
+    dma_dword(a.indices + (int64_t)g * a.topk + max(k, 0), ix_slot(x));
+  }
+  __device__ __forceinline__ int row_j(int x) const {
+    return (a.topk > 0) ? ri_read(ix_slot(x)) : j0 + 32 * x + vrow();
+  }
+  __device__ __forceinline__ void page_fetch(int x) const {  // block-table entries of step x
+    const int j = row_j(x);
+    const int pi = min(max(j >> a.ps_log2, 0), a.max_pages - 1);
+    dma_dword(a.block_table + (int64_t)b * a.max_pages + pi, pg_slot(x));
+  }
+  __device__ __forceinline__ uint64_t row_base(int x, bool* valid) const {
+    const int j = row_j(x);
+    const int page = ri_read(pg_slot(x));
+    const int k = 32 * x + vrow();
+    bool ok = x < qend && k < n && (j >> a.ps_log2) < a.max_pages;
+    if (a.topk > 0) ok = ok && j >= 0 && j < L;
+    ok = ok && page >= 0 && (int64_t)page < a.num_pages;
+    *valid = ok;
+    if (!ok) return (uint64_t)(uintptr_t)a.zero_row;
+    const int slot = j & ((1 << a.ps_log2) - 1);
+    return (uint64_t)(uintptr_t)(a.cache + (int64_t)page * a.page_stride + (int64_t)slot * a.row_bytes);
+  }
+  // Bundle x: value wave v moves rows [8v, 8v + 8) of step x into its slot (one 1 KB row per
+  // instruction, plus the eight RoPE tails in one), the block-table entries of step x + 3 and,
+  // with index lists, the index entries of step x + 6. Every bundle holds the same number of memory
+  // instructions, so "bundle x has landed" is an exact vmcnt. prep() works out the addresses (ring
+  // entries in LDS, the row-valid mask) ahead of time; issue() only sends the transfers.
+  struct Prep {
+    uint64_t base;         // lane l: row 8v + (l & 7) of the step (or the zero row)
+    uint64_t rope;         // lane l: RoPE tail chunk of row 8v + (l >> 3), swizzled
+    const int32_t* page;   // block-table entry of step x + 3's row
+  };
+  __device__ __forceinline__ Prep prep(int x) const {
+    Prep p;
+    bool v;
+    p.base = row_base(x, &v);
+    const uint32_t m = (uint32_t)__ballot(v) & 0xFFu;
+    if (lane == 0) *reinterpret_cast<LDS_AS uint8_t*>(sm + kMOff + 4 * (x & 3) + (wave - 4)) = (uint8_t)m;
+    if constexpr (HAS_B) {
+      const int r = 8 * (wave - 4) + (lane >> 3);
+      const int c = (lane & 7) ^ swz_b(r);
+      const uint32_t lo = __shfl((uint32_t)p.base, lane >> 3, 64);
+      const uint32_t hi = __shfl((uint32_t)(p.base >> 32), lane >> 3, 64);
+      p.rope = (((uint64_t)hi << 32) | lo) + 1024 + 16 * c;
+    } else {
+      p.rope = 0;
+    }
+    const int j = row_j(x + 3);
+    const int pi = min(max(j >> a.ps_log2, 0), a.max_pages - 1);
+    p.page = a.block_table + (int64_t)b * a.max_pages + pi;
+    return p;
+  }
+  __device__ __forceinline__ void issue(int x, const Prep& p) const {
+    // slot x % 3; the block-table entries of step x + 3 go into ring slot (x + 3) & 3
+    const uint32_t sa = slot_of(x);
+    const int r0 = 8 * (wave - 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      dma_x4s<true>(16 * lane, readlane64(p.base, i), lds_addr(sm + sa + (r0 + i) * kRowStrideA));
+    if constexpr (HAS_B)
+      dma_x4<true>(reinterpret_cast<const void*>((uintptr_t)p.rope), lds_addr(sm + sa + kSlotA + (wave - 4) * 1024));
+    dma_dword(p.page, pg_slot(x + 3));
+    if (a.topk > 0) idx_fetch(x + 6);
+  }
+
+  __device__ __forceinline__ void load_split(int s) {
+    cur_split = s;
+    const int32_t* plan = a.plan;
+    const int32_t* rec = plan + a.splits_off + 4 * (int64_t)s;
+    g = __builtin_amdgcn_readfirstlane(rec[0]);
+    const int kb = __builtin_amdgcn_readfirstlane(rec[1]), ke = __builtin_amdgcn_readfirstlane(rec[2]);
+    j0 = __builtin_amdgcn_readfirstlane(plan[a.grp_rows_off + 2 * g]);
+    n = __builtin_amdgcn_readfirstlane(plan[a.grp_rows_off + 2 * g + 1]);
+    nsplit = __builtin_amdgcn_readfirstlane(plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g]);
+    b = (a.topk > 0) ? g / a.Sq : g;
+    L = __builtin_amdgcn_readfirstlane(a.seqlens[b]);
+    q0 = 2 * kb;
+    qend = min(2 * ke, (n + kRows - 1) / kRows);  // steps holding at least one row
+  }
+
+  // ===== score waves ===========================================================================
+  __device__ void score_split(int mt) {
+    const int s = wave;
+    const bool sparse = a.topk > 0;
+    // Q^T of the wave's two 16-row tiles: latent k steps into registers for the whole split; the
+    // RoPE part of all its 32 rows into LDS (rows past R repeat the last row; their outputs are
+    // dropped)
+    bf16x8 qr[2][KSQ];
+    {
+      const int nl = lane & 15, gl = lane >> 4;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int qrow = mt * 128 + 32 * s + 16 * nt + nl;
+        const int r = min(qrow, a.R - 1);
+        const bf16x8* src = reinterpret_cast<const bf16x8*>(a.q + ((int64_t)g * a.R + r) * DQK + 8 * gl);
+#pragma unroll
+        for (int ks = 0; ks < KSQ; ++ks) qr[nt][ks] = src[4 * ks];
+      }
+    }
+    if constexpr (HAS_B) {
+      // eight rows of 128 bytes per LDS-DMA instruction; lane l brings chunk (l & 7) ^ swz(row) of
+      // row (l >> 3), so the LDS copy is swizzled like the RoPE tails of the KV rows
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int row = 32 * s + 8 * k + (lane >> 3);  // row of the tile
+        const int r = min(mt * 128 + row, a.R - 1);
+        const uint16_t* src = a.q + ((int64_t)g * a.R + r) * DQK + 512 + 8 * ((lane & 7) ^ swz_b(row));
+        dma_x4(src, lds_addr(sm + kQrOff + (32 * s + 8 * k) * 128));
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) asm volatile("" : "+v"(qr[nt][ks]));
+    f32x4 o[8][2];  // O^T of the own rows: [output column tile][row tile]; the first step's
+                    // MFMAs write it with a zero accumulator
+    const bool dense_mask = !sparse && (a.causal || a.window > 0);
+    float m_ref[2] = {kNegInf, kNegInf}, l_acc[2] = {0.f, 0.f};
+    float m_top[2] = {kNegInf, kNegInf};  // MAXL: the rows' true maxima (m_ref trails them by up to kTau)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q RoPE part in LDS
+    lds_barrier();  // B_q0: counters cleared, Q RoPE part written
+
+    for (int t = q0; t < qend; ++t) {
+      const int ln = opaque_lane();
+      const int nl = ln & 15, gl = ln >> 4;
+      const int k = t - q0;  // step index within the split
+      wait4(kCLanded, k + 1);  // rows of step t in LDS
+      const uint32_t sa = slot_of(t);
+      const uint32_t sb = sa + kSlotA;
+      bf16x8 pf[2];
+      float alpha[2] = {1.f, 1.f};
+      bool any_up = false;
+      {
+        // ---- S^T = K Q^T: 32 step rows x the wave's 32 rows ---------------------------------
+        const uint32_t kaddr = sa + nl * kRowStrideA + 16 * gl;
+        auto k_op = [&](int kt, int ks) -> bf16x8 {
+          if (ks < 16) return lds_read_b128(sm, kaddr + 16 * kt * kRowStrideA + 64 * ks);
+          const int row = 16 * kt + nl;
+          const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
+          return lds_read_b128(sm, sb + row * 128 + 16 * c);
+        };
+        auto q_rope = [&](int nt, int ks) -> bf16x8 {  // RoPE k steps of Q^T, from LDS
+          const int row = 32 * s + 16 * nt + nl;
+          const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
+          return lds_read_b128(sm, kQrOff + row * 128 + 16 * c);
+        };
+        constexpr int D = 2;  // operand steps in flight
+        bf16x8 ka[D][2];
+#pragma unroll
+        for (int i = 0; i < D - 1; ++i)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) ka[i][kt] = k_op(kt, i);
+        f32x4 sacc[2][2];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + D - 1 < KS) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) ka[(ks + D - 1) % D][kt] = k_op(kt, ks + D - 1);
+          }
+          if (ks < KSQ) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int nt = 0; nt < 2; ++nt) {
+                if (ks == 0) mfma_vv0(sacc[kt][nt], ka[ks % D][kt], qr[nt][ks]);
+                else mfma_vv(sacc[kt][nt], ka[ks % D][kt], qr[nt][ks]);
+              }
+          } else {
+            const bf16x8 qa = q_rope(0, ks), qb = q_rope(1, ks);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              mfma_vv(sacc[kt][0], ka[ks % D][kt], qa);
+              mfma_vv(sacc[kt][1], ka[ks % D][kt], qb);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);  // keep the operand loads D - 1 steps ahead only
+        }
+        mfma_drain4(sacc[0][0], sacc[0][1], sacc[1][0], sacc[1][1]);
+
+        // ---- masks ---------------------------------------------------------------------------
+        const bool tail = 32 * (t + 1) > n;
+        const uint32_t vmask = *reinterpret_cast<const LDS_AS uint32_t*>(sm + kMOff + 4 * (t & 3));
+        const bool need_mask = sparse ? (vmask != ~0u) : (tail || dense_mask);
+        if (need_mask) {
+          // step row c = 16 kt + e of the lane's group: valid iff (sparse) its mask bit is set, or
+          // (dense) its position j = j0 + 32 t + 4 gl + c is inside the group's rows and the query
+          // row's causal / window range; every test is a register against an immediate
+          if (sparse) {
+            const uint32_t vm = vmask >> (4 * gl);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const bool ok = ((vm >> (16 * kt + e)) & 1u) != 0;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) sacc[kt][nt][e] = ok ? sacc[kt][nt][e] : kNegInf;
+              }
+          } else {
+            const int kbase = 32 * t + 4 * gl;        // step offset of c = 0
+            const int nrem = n - kbase;                // c < nrem
+            int hi[2], lo[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+              // the query's position pos = L - Sq + token (token = row / H), in units of c
+              const int qrow = mt * 128 + 32 * s + 16 * nt + nl;
+              const int rel = L - a.Sq + qrow / a.H - j0 - kbase;
+              hi[nt] = a.causal ? rel : (1 << 30);
+              lo[nt] = a.window > 0 ? rel - a.window + 1 : -(1 << 30);
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int c = 16 * kt + e;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                  const bool ok = (c < nrem) & (c <= hi[nt]) & (c >= lo[nt]);
+                  sacc[kt][nt][e] = ok ? sacc[kt][nt][e] : kNegInf;
+                }
+              }
+          }
+        }
+
+        // ---- softmax of the wave's rows (base 2, lazy reference maximum) ---------------------
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          float mx = kNegInf;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kt][nt][e]);
+          mx = rows_max(mx);
+          const float mnew = mx * a.scale_log2;  // -inf stays -inf (scale > 0)
+          if constexpr (MAXL) m_top[nt] = fmaxf(m_top[nt], mnew);
+          if (mnew > m_ref[nt] + kTau) {
+            alpha[nt] = __builtin_amdgcn_exp2f(m_ref[nt] - mnew);  // m_ref = -inf -> 0
+            m_ref[nt] = mnew;
+            l_acc[nt] *= alpha[nt];
+            any_up = true;
+          }
+          const float mu = (m_ref[nt] == kNegInf) ? 0.f : m_ref[nt];
+          float lsum = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][nt][e], a.scale_log2, -mu));
+              lsum += pv;
+              pf[nt][kt * 4 + e] = (__bf16)pv;
+            }
+          l_acc[nt] += lsum;
+        }
+      }
+      // ---- publish P^T of step t and its rescale factors into buffer t & 1, once the value waves
+      // hold P^T of step t - 2 (the buffer's previous contents) ---------------------------------
+      const uint32_t pb = (uint32_t)(t & 1);
+      const bool wave_up = __any(any_up);
+      wait4(kCPConsumed, k - 1);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        *reinterpret_cast<LDS_AS bf16x8*>(sm + kPOff + pb * 8192 + ((2 * s + nt) * 64 + ln) * 16) = pf[nt];
+        if (gl == 0) *reinterpret_cast<LDS_AS float*>(sm + kAOff + pb * 512 + 4 * (32 * s + 16 * nt + nl)) = alpha[nt];
+      }
+      if (ln == 0) *reinterpret_cast<LDS_AS int*>(sm + kFOff + pb * 16 + 4 * s) = wave_up ? 1 : 0;
+      signal(kCPReady, s, k + 1);
+      // ---- own rows: rescale, then O^T += V^T P^T for columns [128s, 128s + 128) --------------
+      const bool first = (k == 0);
+      if (wave_up && !first) {
+        mfma_drain_v(o);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) o[ct][nt] *= alpha[nt];
+          asm volatile("" : "+v"(o[ct][0]), "+v"(o[ct][1]));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      const uint32_t vbase = sa + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (ln & 3) + 2 * (128 * s);
+      auto v_op = [&](int ct) -> bf16x8 {
+        const uint32_t ad = vbase + 32 * ct;
+        const bf16x4 v0 = lds_read_tr(sm, ad);
+        const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 va[8];  // every V^T operand of the step in flight at once (QK^T's registers are free)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) va[ct] = v_op(ct);
+      asm volatile("s_nop 4" ::: "memory");  // P^T written by VALU, O^T rescaled: wait states
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        if (first) {
+          mfma_vv0(o[ct][0], va[ct], pf[0]);
+          mfma_vv0(o[ct][1], va[ct], pf[1]);
+        } else {
+          mfma_vv(o[ct][0], va[ct], pf[0]);
+          mfma_vv(o[ct][1], va[ct], pf[1]);
+        }
+      }
+      signal(kCReleased, s, k + 1);  // rows of step t read for the last time by this wave
+    }
+    mfma_drain_v(o);
+    const int ln = opaque_lane();
+    const int nl = ln & 15, gl = ln >> 4;
+    // ---- row statistics for the value waves ----------------------------------------------------
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float lt = rows_sum(l_acc[nt]);
+      const int hrow = 32 * s + 16 * nt + nl;
+      if (gl == 0) {
+        *reinterpret_cast<LDS_AS float*>(sm + kLOff + 4 * hrow) = lt;
+        *reinterpret_cast<LDS_AS float*>(sm + kLOff + 512 + 4 * hrow) = m_ref[nt];
+        const int r = mt * 128 + hrow;
+        if (MAXL && r < a.R) {  // natural-log units of the scaled scores
+          const float ml = m_top[nt] * 0.69314718055994530942f;
+          if (nsplit == 1) a.max_logits[lse_index(r)] = ml;
+          else a.part_max[(int64_t)cur_split * a.R + r] = ml;
+        }
+      }
+      l_acc[nt] = lt;
+    }
+    lds_barrier();  // E1: statistics published; every transfer has landed
+    // ---- own rows: normalise into the staging rows, LSE -----------------------------------------
+    const bool final_out = (nsplit == 1);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int hrow = 32 * s + 16 * nt + nl;
+      const int r = mt * 128 + hrow;
+      float lse_nat, scale;
+      row_norm(min(r, a.R - 1), m_ref[nt], l_acc[nt], final_out, &lse_nat, &scale);
+      const uint32_t row_at = hrow * kStageRow + 2 * (128 * s + 4 * gl);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const f32x4 v = o[ct][nt] * scale;
+        const u32x2 w = {(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                         (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
+        *reinterpret_cast<LDS_AS u32x2*>(sm + row_at + 32 * ct) = w;
+      }
+      if (gl == 0 && r < a.R) {
+        if (final_out) a.lse[lse_index(r)] = lse_nat;
+        else a.part_lse[(int64_t)cur_split * a.R + r] = lse_nat;
+      }
+    }
+    lds_barrier();  // E2: output rows staged
+    store_rows(mt);
+    lds_barrier();  // E3: staging area and slots reused by the next split
+  }
+
+  // Output rows of the tile leave LDS as whole 1 KB rows: wave w stores rows [16w, 16w + 16).
+  __device__ __forceinline__ void store_rows(int mt) {
+    const int s = cur_split;
+    const bool final_out = (nsplit == 1);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int hrow = 16 * wave + rr;
+      const int r = mt * 128 + hrow;
+      if (r < a.R) {
+        const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(sm + hrow * kStageRow + 16 * lane);
+        uint16_t* dst = final_out ? a.out + ((int64_t)g * a.R + r) * kDv : a.part_o + ((int64_t)s * a.R + r) * kDv;
+        *reinterpret_cast<u32x4*>(dst + 8 * lane) = v;
+      }
+    }
+  }
+
+  // ===== value waves ===========================================================================
+  __device__ void value_split(int mt) {
+    const int vw = wave - 4;  // the SIMD's score wave index
+    const bool sparse = a.topk > 0;
+    __builtin_assume(vw >= 0 && vw < 4);
+    f32x4 o[8][6];  // O^T of the other 96 rows: [output column tile][row tile jj]; the first
+                    // accumulated step writes it with a zero accumulator
+    // row tile jj of this wave = row tile j of the workgroup, skipping the score wave's own two
+    auto tile_of = [&](int jj) -> int { return jj + (jj >= 2 * vw ? 2 : 0); };
+
+    // ---- prologue: row entries of the first steps, bundles q0 .. q0 + 2 ------------------------
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // rings free
+    if (wave == 4 && lane < 20) *reinterpret_cast<LDS_AS int*>(sm + kCOff + 4 * lane) = 0;  // counters
+    if (sparse) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) idx_fetch(q0 + i);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) page_fetch(q0 + i);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    issue(q0, prep(q0));
+    issue(q0 + 1, prep(q0 + 1));
+    issue(q0 + 2, prep(q0 + 2));
+    lds_barrier();  // B_q0: counters cleared
+    // bundle q0 landed (bundles q0 + 1, q0 + 2 may be in flight)
+    if (sparse) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * (kDmaOps + 2)) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * (kDmaOps + 1)) : "memory");
+    signal(kCLanded, vw, 1);
+
+    for (int t = q0; t < qend; ++t) {
+      const int k = t - q0;
+      // bundle t + 1 landed (bundle t + 2 may be in flight): its rows are the score waves' next
+      if (sparse) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaOps + 2) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaOps + 1) : "memory");
+      signal(kCLanded, vw, k + 2);
+      const Prep next = prep(t + 3);  // addresses of bundle t + 3 (their LDS reads overlap the wait)
+      // ---- step t: P^T, flags and rescale factors once the score waves have published them -----
+      wait4(kCPReady, k + 1);
+      const int ln = opaque_lane();
+      const int nl = ln & 15, gl = ln >> 4;
+      const uint32_t pbo = (uint32_t)(t & 1);
+      const LDS_AS int* fl = reinterpret_cast<const LDS_AS int*>(sm + kFOff + pbo * 16);
+      const int f0 = fl[0], f1 = fl[1], f2 = fl[2], f3 = fl[3];
+      const int fmask = ((f0 ? 1 : 0) | (f1 ? 2 : 0) | (f2 ? 4 : 0) | (f3 ? 8 : 0)) & ~(1 << vw);
+      const bool first = (k == 0);
+      bf16x8 pb[6];
+#pragma unroll
+      for (int jj = 0; jj < 6; ++jj)
+        pb[jj] = *reinterpret_cast<const LDS_AS bf16x8*>(sm + kPOff + pbo * 8192 + (tile_of(jj) * 64 + ln) * 16);
+      float al[6];
+      if (fmask && !first) {
+#pragma unroll
+        for (int jj = 0; jj < 6; ++jj)
+          al[jj] = *reinterpret_cast<const LDS_AS float*>(sm + kAOff + pbo * 512 + 4 * (16 * tile_of(jj) + nl));
+      }
+      signal(kCPConsumed, vw, k + 1);  // P^T buffer t & 1 may be overwritten (with step t + 2)
+      if (fmask && !first) {
+        // only the row tiles whose score wave moved its reference maximum
+        mfma_drain_v(o);
+#pragma unroll
+        for (int jj = 0; jj < 6; ++jj) {
+          if (!((fmask >> (tile_of(jj) >> 1)) & 1)) continue;
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct) {
+            o[ct][jj] *= al[jj];
+            asm volatile("" : "+v"(o[ct][jj]));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        asm volatile("s_nop 4" ::: "memory");
+      }
+      const uint32_t vbase = slot_of(t) + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (ln & 3) + 2 * (128 * vw);
+      auto v_op = [&](int ct) -> bf16x8 {
+        const uint32_t ad = vbase + 32 * ct;
+        const bf16x4 v0 = lds_read_tr(sm, ad);
+        const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      constexpr int VD = 3;
+      bf16x8 va[VD];
+#pragma unroll
+      for (int i = 0; i < VD - 1; ++i) va[i] = v_op(i);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        if (ct + VD - 1 < 8) va[(ct + VD - 1) % VD] = v_op(ct + VD - 1);
+        if (first) {
+#pragma unroll
+          for (int jj = 0; jj < 6; ++jj) mfma_vv0(o[ct][jj], va[ct % VD], pb[jj]);
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 6; ++jj) mfma_vv(o[ct][jj], va[ct % VD], pb[jj]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      signal(kCReleased, 4 + vw, k + 1);  // rows of step t read for the last time by this wave
+      // ---- bundle t + 3 into the slot of step t, once all eight waves have released it ---------
+      wait8(kCReleased, k + 1);
+      issue(t + 3, next);
+    }
+    // the last bundles (zero-row reads) must land before the slots are reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    mfma_drain_v(o);
+    lds_barrier();  // E1: score waves' statistics published
+
+    // ---- epilogue: normalise the 96 rows x 128 columns into the staging rows ------------------
+    const int ln = opaque_lane();
+    const int nl = ln & 15, gl = ln >> 4;
+    const bool final_out = (nsplit == 1);
+#pragma unroll
+    for (int jj = 0; jj < 6; ++jj) {
+      const int hrow = 16 * tile_of(jj) + nl;
+      const int r = mt * 128 + hrow;
+      const float lt = *reinterpret_cast<const LDS_AS float*>(sm + kLOff + 4 * hrow);
+      const float m2 = *reinterpret_cast<const LDS_AS float*>(sm + kLOff + 512 + 4 * hrow);
+      float lse_nat, scale;
+      row_norm(min(r, a.R - 1), m2, lt, final_out, &lse_nat, &scale);
+      const uint32_t row_at = hrow * kStageRow + 2 * (128 * vw + 4 * gl);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const f32x4 v = o[ct][jj] * scale;
+        const u32x2 w = {(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                         (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
+        *reinterpret_cast<LDS_AS u32x2*>(sm + row_at + 32 * ct) = w;
+      }
+    }
+    lds_barrier();  // E2: output rows staged
+    store_rows(mt);
+    lds_barrier();  // E3: staging area and slots reused by the next split
+  }
+
+  // LSE (natural log) and output scale of a row; the sink is folded in for final outputs.
+  __device__ __forceinline__ void row_norm(int r, float m2, float l, bool final_out, float* lse_nat,
+                                           float* scale) const {
+    const float kLn2 = 0.69314718055994530942f;
+    if (l > 0.f) {
+      float lse = (m2 + __log2f(l)) * kLn2;
+      float sc = 1.f / l;
+      if (final_out && a.sink != nullptr) {
+        const float sk = a.sink[(a.topk > 0) ? r : r % a.H];
+        const float mx = fmaxf(lse, sk);
+        const float lse2 = mx + __logf(__expf(lse - mx) + __expf(sk - mx));
+        sc *= __expf(lse - lse2);
+        lse = lse2;
+      }
+      *lse_nat = lse;
+      *scale = sc;
+    } else {
+      *scale = 0.f;
+      *lse_nat = (final_out && a.sink != nullptr) ? a.sink[(a.topk > 0) ? r : r % a.H] : kNegInf;
+    }
+  }
+  __device__ __forceinline__ int64_t lse_index(int r) const {
+    int bb, t, h;
+    if (a.topk > 0) {
+      bb = g / a.Sq;
+      t = g % a.Sq;
+      h = r;
+    } else {
+      bb = g;
+      t = r / a.H;
+      h = r % a.H;
+    }
+    return ((int64_t)bb * a.H + h) * a.Sq + t;
+  }
+};
+
 // Workgroup b -> (unit, row tile): all row tiles of a unit land on the same XCD (workgroups are
 // dealt to the 8 XCDs round-robin), so the second reader of a KV block finds it in that L2.
 __device__ __forceinline__ void unit_tile(int bid, int m_tiles, int* unit, int* mt) {
@@ -1330,6 +1996,39 @@ void decode_spec64_kernel(DecodeArgs a) {
     for (int s = s0; s < s1; ++s) {
       d.load_split(s);
       d.value_split(s, mt);
+    }
+  }
+}
+
+// Workgroup b -> (unit, row tile) for the 128-row kernel: workgroups are dealt to the 8 XCDs
+// round-robin; XCD x takes units [x * per, (x + 1) * per), all row tiles of a unit together, so the
+// splits of one request (consecutive units) share one L2 for their Q rows and block-table entries.
+__device__ __forceinline__ void unit_tile_blocked(int bid, int m_tiles, int per, int* unit, int* mt) {
+  const int x = bid & 7, q = bid >> 3;
+  *mt = q % m_tiles;
+  *unit = x * per + q / m_tiles;
+}
+
+template <int DQK, bool MAXL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_spec128_kernel(DecodeArgs a, int per) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Spec128<DQK, MAXL>::LDS];
+  const lds_ptr base = (lds_ptr)lds;
+  int unit, mt;
+  unit_tile_blocked(blockIdx.x, a.m_tiles, per, &unit, &mt);
+  if (unit >= a.U || !plan_matches(a.plan, a.G, a.U, a.R)) return;
+  const int s0 = a.plan[a.unit_ptr_off + unit];
+  const int s1 = a.plan[a.unit_ptr_off + unit + 1];
+  Spec128<DQK, MAXL> d(a, base);
+  if (d.wave < 4) {
+    for (int s = s0; s < s1; ++s) {
+      d.load_split(s);
+      d.score_split(mt);
+    }
+  } else {
+    for (int s = s0; s < s1; ++s) {
+      d.load_split(s);
+      d.value_split(mt);
     }
   }
 }
@@ -1370,7 +2069,21 @@ hipError_t launch_spec64(DecodeArgs a, hipStream_t s) {
 }
 
 template <int DQK>
+hipError_t launch_spec128(DecodeArgs a, hipStream_t s) {
+  a.m_tiles = (a.R + 127) / 128;
+  const int per = (a.U + 7) / 8;
+  const int64_t grid = (int64_t)8 * per * a.m_tiles;
+  if (grid <= 0) return hipSuccess;
+  if (a.max_logits != nullptr)
+    hipLaunchKernelGGL((decode_spec128_kernel<DQK, true>), dim3((unsigned)grid), dim3(512), 0, s, a, per);
+  else
+    hipLaunchKernelGGL((decode_spec128_kernel<DQK, false>), dim3((unsigned)grid), dim3(512), 0, s, a, per);
+  return hipGetLastError();
+}
+
+template <int DQK>
 hipError_t launch_dqk(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
+  if (sh.fmt == 0 && sh.R > 64) return launch_spec128<DQK>(a, s);  // bf16 rows, 65+ stacked rows
   if (sh.fmt != 0) return launch_spec64<DQK, true>(a, s);  // fp8 rows: 64-row tiles for any R
   if (a.max_logits == nullptr) {  // the per-row maximum is produced by the 64-row kernel only
     if (sh.R <= 16) return launch_cfg<Cfg<16, 4, DQK>>(a, s);

@@ -43,7 +43,8 @@ struct PlanLayout {
 inline void tile_params(int R, int* m_tile, int* fixed) {
   if (R <= 16) { *m_tile = 16; *fixed = 3; }
   else if (R <= 32) { *m_tile = 32; *fixed = 2; }
-  else { *m_tile = 64; *fixed = 4; }
+  else if (R <= 64) { *m_tile = 64; *fixed = 4; }
+  else { *m_tile = 128; *fixed = 4; }
 }
 
 struct Shape {  // derived, validated problem shape

@@ -15,7 +15,8 @@ Definitions
     dense                 -> n = L, j0 = 0
 - Blocks of 64 rows: nblk_g = ceil(n_g / 64).
 - Kernel tile: M_TILE query rows per workgroup and FIXED (per-split overhead in block units) come
-  from R: R <= 16 -> (16, 3); R <= 32 -> (32, 2); otherwise (64, 4). m_tiles = ceil(R / M_TILE).
+  from R: R <= 16 -> (16, 3); R <= 32 -> (32, 2); R <= 64 -> (64, 4); otherwise (128, 4).
+  m_tiles = ceil(R / M_TILE).
 - Work units: U = max(1, num_cus // m_tiles), num_cus being the compute units planned for.
 - Cost: cost_g = nblk_g + FIXED if nblk_g > 0 else 0; P_g = exclusive prefix sum of cost;
   total = sum of cost; quota = max(1, ceil(total / U)).
@@ -51,7 +52,9 @@ def tile_params(R: int):
         return 16, 3
     if R <= 32:
         return 32, 2
-    return 64, 4
+    if R <= 64:
+        return 64, 4
+    return 128, 4
 
 
 def group_rows(seqlens: Sequence[int], q_len: int, topk: int, window: int,

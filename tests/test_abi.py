@@ -59,15 +59,15 @@ def test_workspace_sizes(lib):
     words = 16 + (G + 1) + (U + 1) + 2 * G + 4 * (G + U)
     assert plan_b == ((words * 4 + 255) // 256) * 256 + 2048
     assert part_b == (G + U) * 16 * (512 * 2 + 4)
-    # 128 heads: two 64-row tiles per group, U = cus / 2
+    # 128 heads: one 128-row tile per group, U = cus
     rc, _, part_b = ws(good(num_heads=128), 256)
-    assert rc == 0 and part_b == (2 + 128) * 128 * (512 * 2 + 4)
-    # 4 tokens x 64 heads = 256 rows -> 4 tiles, U = 64
+    assert rc == 0 and part_b == (2 + 256) * 128 * (512 * 2 + 4)
+    # 4 tokens x 64 heads = 256 rows -> 2 tiles of 128, U = 128
     rc, _, part_b = ws(good(num_heads=64, q_len=4, causal=1, window=128), 256)
-    assert rc == 0 and part_b == (2 + 64) * 256 * (512 * 2 + 4)
+    assert rc == 0 and part_b == (2 + 128) * 256 * (512 * 2 + 4)
     # index lists: groups are (request, token) pairs of H rows
     rc, _, part_b = ws(good(num_heads=128, q_len=2, topk=64), 256)
-    assert rc == 0 and part_b == (4 + 128) * 128 * (512 * 2 + 4)
+    assert rc == 0 and part_b == (4 + 256) * 128 * (512 * 2 + 4)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -212,7 +212,7 @@ def test_sparse_prefill_host_checks(lib):
     rc, plan_b, part_b = ws(p, cus)
     assert rc == 0
     r256 = lambda x: (x + 255) // 256 * 256
-    U = cus // ((H + 63) // 64)
+    U = cus // ((H + 127) // 128)  # 128-row tiles above 64 heads
     expect = r256(r256(r256(4 * (1 + pages)) + plan_b) + part_b) + (s_q + U) * H * 4
     assert n.value == expect
     # sizes out of range
