@@ -720,6 +720,9 @@ __device__ __forceinline__ void mfma_s0(f32x4& c, const bf16x8& a, const bf16x8&
 __device__ __forceinline__ void mfma_o(f32x4& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
+__device__ __forceinline__ void mfma_o0(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&a"(c) : "v"(a), "v"(b));
+}
 // 19 wait states: more than an XDL write -> VALU read of a 16x16x32 MFMA result needs.
 __device__ __forceinline__ void mfma_drain4(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& c3) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
@@ -770,6 +773,24 @@ __device__ __forceinline__ void mfma_sq2_cvt_last(f32x4& c0, f32x4& c1, const bf
       "s_nop 7\n\ts_nop 7\n\ts_nop 2"
       : "+v"(c0), "+v"(c1)
       : "v"(a0), "v"(a1), "a"(b));
+}
+// Global stores as inline assembly: the compiler's wait-count pass does not see them, so it does
+// not make later register writes wait for them (with the LDS-DMA transfers in flight, such a wait
+// would also hold for every transfer). One wait state after each guards the store-data hazard.
+__device__ __forceinline__ void st_global_b128(void* p, const u32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_global_b32(void* p, float v) {
+  asm volatile("global_store_dword %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
+}
+// An accumulator tile read into VGPRs by explicit copies: the tile stays an accumulation-register
+// value for the compiler (a plain VALU use would make it re-home the whole array).
+__device__ __forceinline__ f32x4 acc_read(const f32x4& o) {
+  f32x4 v;
+  asm volatile("v_accvgpr_read_b32 %0, %4\n\tv_accvgpr_read_b32 %1, %5\n\tv_accvgpr_read_b32 %2, %6\n\tv_accvgpr_read_b32 %3, %7"
+               : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3])
+               : "a"(o[0]), "a"(o[1]), "a"(o[2]), "a"(o[3]));
+  return v;
 }
 template <int N, int M>
 __device__ __forceinline__ void mfma_drain_acc(f32x4 (&o)[N][M]) {
@@ -1303,644 +1324,726 @@ struct Spec64 {
   }
 };
 
-// VGPR-only MFMA forms for the 128-row kernel. A kernel that holds anything in accumulation
-// registers gets its 256 registers per wave split evenly between the two files; this one needs
-// about 200 registers of long-lived accumulators and operands and 50 of temporaries, so it keeps
-// everything in the 256 architectural VGPRs (MFMAs read and write them directly).
-__device__ __forceinline__ void mfma_vv(f32x4& c, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_vv0(f32x4& c, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
-}
-template <int N, int M>
-__device__ __forceinline__ void mfma_drain_v(f32x4 (&o)[N][M]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < N; ++i)
-#pragma unroll
-    for (int k = 0; k < M; ++k) asm volatile("" : "+v"(o[i][k]));
-}
-
-// 128 query rows per workgroup (all heads of a DeepSeek-V3 request, so every KV row is taken in by
-// one CU only), eight waves in two roles, two waves per SIMD:
-//  * score wave s (waves 0-3): QK^T and the softmax of query rows [32s, 32s + 32) of the tile (the
-//    latent part of Q^T held in registers, its RoPE part in LDS), and PV of those rows for output
-//    columns [128s, 128s + 128), one step behind like the value waves;
-//  * value wave s (waves 4-7, on the SIMD of score wave s): PV of the other 96 rows for output
-//    columns [128s, 128s + 128), one step behind the score waves, plus every global -> LDS
-//    transfer (rows with the streaming cache policy: each row is read once).
-// MAXL: also track each row's true maximum score (the max_logits output).
-// Inside a split the two roles are ordered by counters in LDS, not workgroup barriers, so the score
-// waves can run QK^T of step t + 1 while the value waves accumulate step t:
-//  * LANDED: a value wave signals when its rows of a step have arrived; the score waves start step
-//    t once all four have (for step t);
-//  * PREADY / PCONSUMED: the score waves publish P^T of step t (double-buffered, with its rescale
-//    factors and flags) and signal; the value waves take it into registers and signal; P^T of
-//    step t + 2 overwrites the buffer only after that;
-//  * RELEASED: every wave signals when it has read the rows of step t for the last time; then the
-//    value waves send the rows of step t + 3 into that slot (three slots, so steps t + 1 and t + 2
-//    are landing meanwhile).
-// A wait only ever depends on signals of earlier steps or of the other role's same step that come
-// before its own waits, so no cycle can form.
-template <int DQK, bool MAXL>
-struct Spec128 {
-  static constexpr bool HAS_B = DQK > 512;                 // RoPE region present
-  static constexpr int KS = DQK / 32;                      // 32-wide k steps of QK^T
-  static constexpr int KSQ = 16;                           // k steps of Q^T held in registers
-  static constexpr int kRows = 32;                         // rows per slot / step
+// 128 query rows per workgroup for bf16 rows: all heads of a DeepSeek-V3 request, so every KV row
+// enters one CU once. Four waves, one per SIMD, all in one role: wave w owns query rows
+// [32w, 32w + 32) of the tile for a whole split. It holds their Q^T in registers, computes
+// S^T = K Q^T, the softmax, and O^T += V^T P^T over all 512 output columns. Its 32 x 512 fp32
+// accumulator lives in the 256 accumulation registers, and P^T never leaves the wave. The waves
+// share only the KV rows in LDS, a ring of four 32-row slots, and one workgroup barrier per step.
+//
+// The step loop is software-pipelined so the MFMA pipe has work while the wave does everything
+// else. Iteration k runs QK^T of step k with the softmax of step k - 1 spread between its MFMAs,
+// and the row transfers of step k + 2 spread there too; then PV of step k - 1, with the row
+// addresses of step k + 3 worked out between its MFMAs. Slots k - 1 and k are read in iteration k,
+// k + 1 and k + 2 are landing; the barrier at the top of iteration k both publishes step k's rows
+// and frees the slot of step k - 2 for step k + 2.
+//
+// A unit's splits are taken in chunks of up to kChunk, whose descriptors sit in LDS. Within a
+// chunk the row stream runs on across split boundaries: a boundary costs the epilogue (the wave's
+// rows normalised, staged through the slot just read and stored as whole 128-byte lines) and the
+// load of the next split's Q^T, not a refill of the ring.
+//
+// Step y's bundle holds the LDS-DMA of its rows, the block-table entries of step y + 3 and, with
+// index lists, the index entries of step y + 6. All three travel by LDS-DMA into small per-wave
+// rings, so no register waits on an in-flight load; their addresses are clamped and their values
+// validated when consumed. Bundles past the chunk's last step read the zero row, so every bundle
+// holds the same number of memory instructions and "bundle k has landed" is always the same
+// vmcnt (one later bundle in flight).
+template <int DQK, bool MAXL, bool SPARSE>
+struct Tile128 {
+  static constexpr bool HAS_B = DQK > 512;               // RoPE region present
+  static constexpr int KS = DQK / 32;                    // 32-wide k steps of QK^T
+  static constexpr int kRows = 32;                       // rows per slot / step
+  static constexpr int NS = 4;                           // slots
   static constexpr int kSlotA = kRows * kRowStrideA;
   static constexpr int kSlot = kSlotA + (HAS_B ? kRows * 128 : 0);
   static_assert(kSlot % 256 == 0, "slot bases keep the low byte of in-slot offsets");
-  static constexpr uint32_t kPOff = 3 * kSlot;             // P^T [2 steps][8 row tiles][64 lanes] x 16 B
-  static constexpr uint32_t kQrOff = kPOff + 2 * 8192;     // Q RoPE part [128 rows][128 B], swizzled
-  static constexpr int kStageRow = 1040;                   // output staging rows (epilogue)
-  static constexpr uint32_t kStatOff =                     // above the Q RoPE part and the staging
-      (kQrOff + (HAS_B ? 128 * 128 : 0)) > 128 * kStageRow ? kQrOff + (HAS_B ? 128 * 128 : 0)
-                                                            : 128 * kStageRow;
-  static constexpr uint32_t kAOff = kStatOff;              // rescale factors [2 steps][128]
-  static constexpr uint32_t kFOff = kAOff + 1024;          // rescale flags [2 steps][4]
-  static constexpr uint32_t kCOff = kFOff + 32;            // step counters, one per signalling wave:
-  static constexpr uint32_t kCLanded = kCOff;              //   [4] bundles landed, per value wave
-  static constexpr uint32_t kCPReady = kCOff + 16;         //   [4] P^T published, per score wave
-  static constexpr uint32_t kCPConsumed = kCOff + 32;      //   [4] P^T taken into registers, per value wave
-  static constexpr uint32_t kCReleased = kCOff + 48;       //   [8] steps whose rows a wave has finished
-  static constexpr uint32_t kMOff = kCOff + 80;            // row-valid masks [4 steps][4 bytes]
-  static constexpr uint32_t kLOff = kMOff + 16;            // final l [128], then m [128]
-  static constexpr uint32_t kRiOff = kLOff + 1024;         // per value wave: block-table entries
-  static constexpr int kRiWave = 4 * 32 + 8 * 32;          //   [4][8], index entries [8][8]
-  static constexpr int LDS = kRiOff + 4 * kRiWave;
+  static constexpr uint32_t kPgOff = NS * kSlot;         // block-table entries [4 waves][4 steps][8]
+  static constexpr uint32_t kIxOff = kPgOff + 4 * 4 * 32;  // index entries [4 waves][8 steps][8]
+  static constexpr uint32_t kMOff = kIxOff + 4 * 8 * 32;   // row-valid masks [8 steps][4 waves] bytes
+  static constexpr uint32_t kDOff = kMOff + 32;           // split descriptors [kChunk][8 words]
+  static constexpr int kChunk = 16;
+  static constexpr uint32_t kRbOff = kDOff + kChunk * 32;  // next bundle's row addresses [4 waves][8]
+  static constexpr int LDS = kRbOff + 4 * 64;
   static_assert(LDS <= 160 * 1024, "LDS of one workgroup");
-  static_assert(128 * kStageRow <= kStatOff, "output staging fits below the row statistics");
-  static constexpr int kDmaOps = 8 + (HAS_B ? 1 : 0);      // row LDS-DMA instructions per bundle
+  static constexpr int kStageRow = HAS_B ? 544 : 528;     // epilogue staging: 256 columns + pad
+  static_assert(4 * 16 * kStageRow <= kSlot, "epilogue staging fits in one slot");
+  // memory instructions per bundle: 8 rows, the RoPE tails (+ with index lists the block-table and
+  // index dwords)
+  static constexpr int kNb = 8 + (HAS_B ? 1 : 0) + (SPARSE ? 2 : 0);
+  static constexpr bool sparse = SPARSE;
+  enum { D_G, D_B, D_J0, D_N, D_L, D_Q0, D_QEND, D_NSPLIT };
+
+  // A position in the chunk's step stream: step t of split ci (ci == nc: past the chunk's end).
+  struct Cur {
+    int y;     // step index in the chunk's stream
+    int ci;    // split within the chunk
+    int t;     // step within the split
+    int q0, qend;        // the split's step range
+    int g, b, j0, n, L;  // the split's group, request, first row, row count, request length
+  };
+  // Dense rows of a bundle: the wave's eight rows are consecutive positions j .. j + 7, on at most
+  // two pages, whose block-table entries e0 (page of j) and e1 (page of j + 7) come through the
+  // scalar cache; k is the rows' offset in the group, n the group's row count. Wave-uniform.
+  struct DRows {
+    int e0, e1, j, k, n;
+  };
+  // The bundle's row addresses in closed form: rows i < isplit lie on page e0 (b0 + i row_bytes),
+  // the rest on page e1 (b1 + (i - isplit) row_bytes); rows i >= nvalid read the zero row.
+  struct DAddr {
+    uint64_t b0, b1;
+    int isplit, nvalid;
+  };
+  // Softmax state of the split whose step is being finished, and the step's own values.
+  struct Soft {
+    float m_ref[2], l_acc[2], m_top[2];  // per row tile: reference maximum, sum, true maximum
+    float alpha[2], mu[2], lsum[2], mx[2], mnew[2], part[2];
+    bool up[2];
+    bf16x8 pf[2];  // P^T of the step
+  };
+  // Per-iteration lane constants (one read of the lane index per step).
+  struct Lane {
+    int ln;        // lane
+    uint32_t v16;  // 16 * lane: the lane's byte offset in a 1 KB transfer
+  };
 
   const DecodeArgs& a;
   lds_ptr sm;
-  int lane, wave;
-  int g, b, L, j0, n, q0, qend, nsplit, cur_split;
+  int wave, mt;
+  int num_pages32;  // page count, clamped to the int range (32-bit compares stay scalar)
+  int nc, T;  // splits and steps of the current chunk
 
-  __device__ Spec128(const DecodeArgs& args, lds_ptr base) : a(args), sm(base) {
-    lane = threadIdx.x & 63;
+  __device__ Tile128(const DecodeArgs& args, lds_ptr base, int tile) : a(args), sm(base), mt(tile) {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    num_pages32 = (int)min(a.num_pages, (int64_t)0x7fffffff);
   }
 
-  __device__ __forceinline__ static uint32_t slot_of(int x) { return (uint32_t)(x % 3) * kSlot; }
-  // The lane index as a value the compiler cannot treat as loop-invariant: addresses derived from
-  // it are recomputed in each step (a few VALU instructions) instead of being hoisted and held in
-  // registers across the whole split.
-  __device__ __forceinline__ int opaque_lane() const {
-    int l = lane;
-    asm volatile("" : "+v"(l));
+  // The lane index, read from the hardware each time it is asked for: addresses derived from it
+  // are recomputed where they are used instead of being held in registers (or spilled) for the
+  // whole kernel.
+  __device__ __forceinline__ int lane_id() const {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
     return l;
   }
-  // Step counters in LDS replace workgroup barriers inside a split. Each signalling wave owns one
-  // counter, the number of steps it has completed for that purpose, and writes it (one lane); a
-  // waiting wave polls until the smallest of the counters it depends on has reached a step. The LDS
-  // executes one wave's instructions in issue order, so a counter write cannot overtake the wave's
-  // earlier LDS reads or writes it vouches for; transfers by LDS-DMA are covered by the issuing
-  // wave's vmcnt wait before it signals. (One shared counter would not do: the waves of a role drift
-  // apart by up to a step, and a count could then be reached with one wave's later signal standing
-  // in for another wave's missing earlier one.) Counters are cleared in the split's prologue.
-  __device__ __forceinline__ void signal(uint32_t ctr, int idx, int count) const {
-    asm volatile("" ::: "memory");  // after every LDS access above, in program order
-    if (lane == 0) *reinterpret_cast<volatile LDS_AS int*>(sm + ctr + 4 * idx) = count;
-    asm volatile("" ::: "memory");
+  __device__ __forceinline__ int desc(int ci, int f) const {
+    return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const LDS_AS int*>(sm + kDOff + 32 * ci + 4 * f));
   }
-  // Polled by lane 0 alone (16 bytes per poll, not 1 KB).
-  __device__ __forceinline__ int min4(uint32_t ctr) const {
-    int m = 0;
-    if (lane == 0) {
-      const u32x4 c = *reinterpret_cast<volatile LDS_AS u32x4*>(sm + ctr);
-      m = min(min((int)c[0], (int)c[1]), min((int)c[2], (int)c[3]));
+  __device__ __forceinline__ Cur cur_load(Cur c) const {
+    c.q0 = desc(c.ci, D_Q0);
+    c.t = c.q0;
+    c.qend = desc(c.ci, D_QEND);
+    c.g = desc(c.ci, D_G);
+    c.b = desc(c.ci, D_B);
+    c.j0 = desc(c.ci, D_J0);
+    c.n = desc(c.ci, D_N);
+    c.L = desc(c.ci, D_L);
+    return c;
+  }
+  __device__ __forceinline__ Cur cur_begin() const {
+    Cur c;
+    c.y = 0;
+    c.ci = 0;
+    return cur_load(c);
+  }
+  // the step after c
+  __device__ __forceinline__ Cur cur_next(Cur c) const {
+    ++c.y;
+    if (++c.t >= c.qend) {
+      if (++c.ci < nc) {
+        c = cur_load(c);
+      } else {  // past the chunk: every row invalid
+        c.ci = nc;
+        c.t = 0;
+        c.q0 = 0;
+        c.qend = 1 << 30;
+        c.n = 0;
+      }
     }
-    return __builtin_amdgcn_readfirstlane(m);
-  }
-  __device__ __forceinline__ void wait4(uint32_t ctr, int target) const {
-    while (min4(ctr) < target) __builtin_amdgcn_s_sleep(1);
-  }
-  __device__ __forceinline__ void wait8(uint32_t ctr, int target) const {
-    while (min(min4(ctr), min4(ctr + 16)) < target) __builtin_amdgcn_s_sleep(1);
+    return c;
   }
 
-  // ===== value waves: row description pipeline and DMA =======================================
-  __device__ __forceinline__ int vrow() const { return 8 * (wave - 4) + (lane & 7); }
-  __device__ __forceinline__ uint32_t pg_slot(int x) const {
-    return kRiOff + (wave - 4) * kRiWave + (x & 3) * 32;
+  // ===== descriptors of a chunk ===============================================================
+  // Lane i of wave 0 describes split cb + i: its group, request, first row and row count, the
+  // request's length, its step range and the group's split count.
+  __device__ void build_table(int cb) {
+    const int ln = lane_id();
+    if (wave == 0 && ln < nc) {
+      const int s = cb + ln;
+      const int32_t* plan = a.plan;
+      const int32_t* rec = plan + a.splits_off + 4 * (int64_t)s;
+      const int g = rec[0], kb = rec[1], ke = rec[2];
+      const int j0 = plan[a.grp_rows_off + 2 * g];
+      const int n = plan[a.grp_rows_off + 2 * g + 1];
+      const int ns = plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g];
+      const int b = sparse ? g / a.Sq : g;
+      const int L = a.seqlens[b];
+      const int q0 = 2 * kb;
+      const int qend = min(2 * ke, (n + kRows - 1) / kRows);  // steps holding at least one row
+      LDS_AS int* d = reinterpret_cast<LDS_AS int*>(sm + kDOff + 32 * ln);
+      d[D_G] = g;
+      d[D_B] = b;
+      d[D_J0] = j0;
+      d[D_N] = n;
+      d[D_L] = L;
+      d[D_Q0] = q0;
+      d[D_QEND] = qend;
+      d[D_NSPLIT] = ns;
+    }
   }
-  __device__ __forceinline__ uint32_t ix_slot(int x) const {
-    return kRiOff + (wave - 4) * kRiWave + 128 + (x & 7) * 32;
+
+  // ===== row transfers =========================================================================
+  // Row i (0-7) of the wave's eight rows of a step is row 8w + i of the step.
+  __device__ __forceinline__ uint32_t pg_slot(int y) const { return kPgOff + wave * 128 + (y & 3) * 32; }
+  __device__ __forceinline__ uint32_t ix_slot(int y) const { return kIxOff + wave * 256 + (y & 7) * 32; }
+  __device__ __forceinline__ int ring_read(uint32_t slot, int i) const {
+    return *reinterpret_cast<const LDS_AS int*>(sm + slot + 4 * i);
   }
+  // position of row i of step c (dense: from the cursor; index lists: the index entry in LDS)
+  __device__ __forceinline__ int row_j(Cur c, int i) const {
+    return sparse ? ring_read(ix_slot(c.y), i) : c.j0 + kRows * c.t + 8 * wave + i;
+  }
+  __device__ __forceinline__ const int32_t* idx_src(Cur c) const {
+    const int k = min(kRows * c.t + 8 * wave + (lane_id() & 7), a.topk - 1);
+    const int32_t* p = a.indices + (int64_t)c.g * a.topk + max(k, 0);
+    return c.ci < nc ? p : reinterpret_cast<const int32_t*>(a.zero_row);
+  }
+  __device__ __forceinline__ const int32_t* page_src(Cur c) const {
+    const int pi = min(max(row_j(c, lane_id() & 7) >> a.ps_log2, 0), a.max_pages - 1);
+    const int32_t* p = a.block_table + (int64_t)c.b * a.max_pages + pi;
+    return c.ci < nc ? p : reinterpret_cast<const int32_t*>(a.zero_row);
+  }
+  // Block-table or index entries of one step (lanes 0-7, one dword each).
   __device__ __forceinline__ void dma_dword(const int32_t* src, uint32_t dst) const {
-    if (lane < 8) dma_x1(src, lds_addr(sm + dst));
+    if (lane_id() < 8) dma_x1(src, lds_addr(sm + dst));
   }
-  __device__ __forceinline__ int ri_read(uint32_t slot) const {
-    return *reinterpret_cast<const LDS_AS int*>(sm + slot + 4 * (lane & 7));
+  // Block-table entries of dense bundle c, loaded a step before its transfers.
+  __device__ __forceinline__ DRows dense_rows(Cur c) const {
+    DRows d;
+    d.k = kRows * c.t + 8 * wave;
+    d.j = c.j0 + d.k;
+    d.n = c.n;  // 0 past the chunk: every row invalid
+    const int p0 = min(max(d.j >> a.ps_log2, 0), a.max_pages - 1);
+    const int p1 = min(max((d.j + 7) >> a.ps_log2, 0), a.max_pages - 1);
+    typedef const __attribute__((address_space(4))) int32_t* const_i32p;  // scalar loads
+    const const_i32p bt = (const_i32p)(uintptr_t)a.block_table + (int64_t)c.b * a.max_pages;
+    d.e0 = bt[p0];
+    d.e1 = bt[p1];
+    return d;
   }
-  __device__ __forceinline__ void idx_fetch(int x) const {  // index entries of step x
-    const int k = min(32 * x + vrow(), a.topk - 1);
-    dma_dword(a.indices + (int64_t)g * a.topk + max(k, 0), ix_slot(x));
+  __device__ __forceinline__ uint64_t page_base(int e, uint32_t slot) const {
+    const bool ok = (e >= 0) & (e < num_pages32);
+    const uint64_t addr = (uint64_t)(uintptr_t)a.cache + (uint64_t)(uint32_t)e * (uint64_t)(uint32_t)a.page_stride +
+                          (uint64_t)(slot * (uint32_t)a.row_bytes);
+    return ok ? addr : (uint64_t)(uintptr_t)a.zero_row;
   }
-  __device__ __forceinline__ int row_j(int x) const {
-    return (a.topk > 0) ? ri_read(ix_slot(x)) : j0 + 32 * x + vrow();
+  __device__ __forceinline__ DAddr dense_addr(const DRows& d) const {
+    DAddr r;
+    const int ps = 1 << a.ps_log2;
+    const int in0 = d.j & (ps - 1);
+    r.isplit = min(ps - in0, 8);
+    r.b0 = page_base((d.j >> a.ps_log2) < a.max_pages ? d.e0 : -1, (uint32_t)in0);
+    r.b1 = page_base(((d.j + 7) >> a.ps_log2) < a.max_pages ? d.e1 : -1, 0u);
+    r.nvalid = min(max(d.n - d.k, 0), 8);
+    return r;
   }
-  __device__ __forceinline__ void page_fetch(int x) const {  // block-table entries of step x
-    const int j = row_j(x);
-    const int pi = min(max(j >> a.ps_log2, 0), a.max_pages - 1);
-    dma_dword(a.block_table + (int64_t)b * a.max_pages + pi, pg_slot(x));
+  // Address of dense row i (+ off), or of the zero row (+ off) when the row lies past the group's
+  // rows or its page entry is out of range (then page_base gave the zero row).
+  __device__ __forceinline__ uint64_t drow(const DAddr& r, int i, uint32_t off) const {
+    const uint64_t on0 = r.b0 + (uint64_t)(uint32_t)(i * (int)a.row_bytes);
+    const uint64_t on1 = r.b1 + (uint64_t)(uint32_t)((i - r.isplit) * (int)a.row_bytes);
+    const uint64_t addr = (i < r.isplit) ? on0 : on1;
+    return ((i < r.nvalid) ? addr : (uint64_t)(uintptr_t)a.zero_row) + off;
   }
-  __device__ __forceinline__ uint64_t row_base(int x, bool* valid) const {
-    const int j = row_j(x);
-    const int page = ri_read(pg_slot(x));
-    const int k = 32 * x + vrow();
-    bool ok = x < qend && k < n && (j >> a.ps_log2) < a.max_pages;
-    if (a.topk > 0) ok = ok && j >= 0 && j < L;
-    ok = ok && page >= 0 && (int64_t)page < a.num_pages;
-    *valid = ok;
-    if (!ok) return (uint64_t)(uintptr_t)a.zero_row;
-    const int slot = j & ((1 << a.ps_log2) - 1);
-    return (uint64_t)(uintptr_t)(a.cache + (int64_t)page * a.page_stride + (int64_t)slot * a.row_bytes);
+  // Address of row i of step c, or the zero row (then *ok is false).
+  __device__ __forceinline__ uint64_t row_addr(Cur c, int i, int j, int page, bool* ok) const {
+    const int k = kRows * c.t + 8 * wave + i;
+    bool v = k < c.n && (j >> a.ps_log2) < a.max_pages;
+    if (sparse) v = v && j >= 0 && j < c.L;
+    v = v && page >= 0 && (int64_t)page < a.num_pages;
+    *ok = v;
+    const uint32_t slot = (uint32_t)(j & ((1 << a.ps_log2) - 1));
+    const uint64_t addr = (uint64_t)(uintptr_t)a.cache + (uint64_t)(uint32_t)page * (uint64_t)(uint32_t)a.page_stride +
+                          (uint64_t)(slot * (uint32_t)a.row_bytes);
+    return v ? addr : (uint64_t)(uintptr_t)a.zero_row;
   }
-  // Bundle x: value wave v moves rows [8v, 8v + 8) of step x into its slot (one 1 KB row per
-  // instruction, plus the eight RoPE tails in one), the block-table entries of step x + 3 and,
-  // with index lists, the index entries of step x + 6. Every bundle holds the same number of memory
-  // instructions, so "bundle x has landed" is an exact vmcnt. prep() works out the addresses (ring
-  // entries in LDS, the row-valid mask) ahead of time; issue() only sends the transfers.
-  struct Prep {
-    uint64_t base;         // lane l: row 8v + (l & 7) of the step (or the zero row)
-    uint64_t rope;         // lane l: RoPE tail chunk of row 8v + (l >> 3), swizzled
-    const int32_t* page;   // block-table entry of step x + 3's row
-  };
-  __device__ __forceinline__ Prep prep(int x) const {
-    Prep p;
-    bool v;
-    p.base = row_base(x, &v);
-    const uint32_t m = (uint32_t)__ballot(v) & 0xFFu;
-    if (lane == 0) *reinterpret_cast<LDS_AS uint8_t*>(sm + kMOff + 4 * (x & 3) + (wave - 4)) = (uint8_t)m;
-    if constexpr (HAS_B) {
-      const int r = 8 * (wave - 4) + (lane >> 3);
-      const int c = (lane & 7) ^ swz_b(r);
-      const uint32_t lo = __shfl((uint32_t)p.base, lane >> 3, 64);
-      const uint32_t hi = __shfl((uint32_t)(p.base >> 32), lane >> 3, 64);
-      p.rope = (((uint64_t)hi << 32) | lo) + 1024 + 16 * c;
-    } else {
-      p.rope = 0;
+  // Row addresses of bundle c (into the wave's table in LDS) and the row-valid mask of step c
+  // (for its consumers): lanes 0-7 work out rows 0-7.
+  __device__ __forceinline__ void prepare(Cur c, const Lane& L) const {
+    const int ln = L.ln;
+    const int i = ln & 7;
+    const int pg = ring_read(pg_slot(c.y), i);
+    const int j = row_j(c, i);
+    bool ok;
+    const uint64_t base = row_addr(c, i, j, pg, &ok);
+    const uint32_t m = (uint32_t)__ballot(ok) & 0xFFu;
+    if (ln == 0) *reinterpret_cast<LDS_AS uint8_t*>(sm + kMOff + 4 * (c.y & 7) + wave) = (uint8_t)m;
+    if (ln < 8) *reinterpret_cast<LDS_AS uint64_t*>(sm + kRbOff + wave * 64 + 8 * i) = base;
+  }
+  __device__ __forceinline__ uint64_t rb_read(int i) const {  // row i's address (wave-uniform)
+    return *reinterpret_cast<const LDS_AS uint64_t*>(sm + kRbOff + wave * 64 + 8 * i);
+  }
+  // Transfer s (0-10) of bundle y (page step cp = y + 3, index step cx = y + 6): rows 0-7 (row s's
+  // address read one transfer ahead into `next`), the RoPE tails, then the ring entries.
+  __device__ __forceinline__ void send_part(int s, int y, Cur cp, Cur cx, uint64_t& next, const DAddr& d,
+                                           const Lane& L) const {
+    const uint32_t sa = (uint32_t)(y & (NS - 1)) * kSlot;
+    if constexpr (!SPARSE) {  // dense: addresses from the scalar block-table entries
+      if (s < 8) {
+        dma_x4s<kRowsNT>(L.v16, drow(d, s, 0), lds_addr(sm + sa + (8 * wave + s) * kRowStrideA));
+      } else if (s == 8) {
+        if constexpr (HAS_B) {
+          const int ln = L.ln;
+          const int i2 = ln >> 3;
+          const uint64_t rope = drow(d, i2, 1024 + 16 * ((ln & 7) ^ swz_b(8 * wave + i2)));
+          dma_x4<kRowsNT>(reinterpret_cast<const void*>((uintptr_t)rope), lds_addr(sm + sa + kSlotA + wave * 1024));
+        }
+      }
+      return;
     }
-    const int j = row_j(x + 3);
-    const int pi = min(max(j >> a.ps_log2, 0), a.max_pages - 1);
-    p.page = a.block_table + (int64_t)b * a.max_pages + pi;
-    return p;
+    if (s < 8) {
+      const uint64_t row = readlane64(next, 0);
+      if (s < 7) next = rb_read(s + 1);
+      dma_x4s<kRowsNT>(L.v16, row, lds_addr(sm + sa + (8 * wave + s) * kRowStrideA));
+    } else if (s == 8) {
+      if constexpr (HAS_B) {
+        const int ln = L.ln;
+        const int i2 = ln >> 3;
+        const uint64_t rope = rb_read(i2) + 1024 + 16 * ((ln & 7) ^ swz_b(8 * wave + i2));
+        dma_x4<kRowsNT>(reinterpret_cast<const void*>((uintptr_t)rope), lds_addr(sm + sa + kSlotA + wave * 1024));
+      }
+    } else if (s == 9) {
+      dma_dword(page_src(cp), pg_slot(y + 3));
+    } else if (s == 10) {
+      if (sparse) dma_dword(idx_src(cx), ix_slot(y + 6));
+    }
   }
-  __device__ __forceinline__ void issue(int x, const Prep& p) const {
-    // slot x % 3; the block-table entries of step x + 3 go into ring slot (x + 3) & 3
-    const uint32_t sa = slot_of(x);
-    const int r0 = 8 * (wave - 4);
+  __device__ __forceinline__ void send_all(int y, Cur cp, Cur cx, const DAddr& d, const Lane& L) const {
+    uint64_t next = SPARSE ? rb_read(0) : 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dma_x4s<true>(16 * lane, readlane64(p.base, i), lds_addr(sm + sa + (r0 + i) * kRowStrideA));
-    if constexpr (HAS_B)
-      dma_x4<true>(reinterpret_cast<const void*>((uintptr_t)p.rope), lds_addr(sm + sa + kSlotA + (wave - 4) * 1024));
-    dma_dword(p.page, pg_slot(x + 3));
-    if (a.topk > 0) idx_fetch(x + 6);
+    for (int s = 0; s < 11; ++s) send_part(s, y, cp, cx, next, d, L);
+  }
+  // bundle k landed, bundle k + 1 possibly still in flight
+  __device__ __forceinline__ void wait_landed() const {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kNb) : "memory");
   }
 
-  __device__ __forceinline__ void load_split(int s) {
-    cur_split = s;
-    const int32_t* plan = a.plan;
-    const int32_t* rec = plan + a.splits_off + 4 * (int64_t)s;
-    g = __builtin_amdgcn_readfirstlane(rec[0]);
-    const int kb = __builtin_amdgcn_readfirstlane(rec[1]), ke = __builtin_amdgcn_readfirstlane(rec[2]);
-    j0 = __builtin_amdgcn_readfirstlane(plan[a.grp_rows_off + 2 * g]);
-    n = __builtin_amdgcn_readfirstlane(plan[a.grp_rows_off + 2 * g + 1]);
-    nsplit = __builtin_amdgcn_readfirstlane(plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g]);
-    b = (a.topk > 0) ? g / a.Sq : g;
-    L = __builtin_amdgcn_readfirstlane(a.seqlens[b]);
-    q0 = 2 * kb;
-    qend = min(2 * ke, (n + kRows - 1) / kRows);  // steps holding at least one row
+  // ===== compute ===============================================================================
+  // Q^T of the wave's two 16-row tiles of group g (rows past R repeat the last row; their outputs
+  // are dropped)
+  __device__ __forceinline__ void load_q(bf16x8 (&qr)[2][KS], int g) const {
+    const int ln = lane_id();
+    const int nl = ln & 15, gl = ln >> 4;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = min(mt * 128 + 32 * wave + 16 * nt + nl, a.R - 1);
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(a.q + ((int64_t)g * a.R + r) * DQK + 8 * gl);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qr[nt][ks] = src[4 * ks];
+    }
   }
 
-  // ===== score waves ===========================================================================
-  __device__ void score_split(int mt) {
-    const int s = wave;
-    const bool sparse = a.topk > 0;
-    // Q^T of the wave's two 16-row tiles: latent k steps into registers for the whole split; the
-    // RoPE part of all its 32 rows into LDS (rows past R repeat the last row; their outputs are
-    // dropped)
-    bf16x8 qr[2][KSQ];
-    {
-      const int nl = lane & 15, gl = lane >> 4;
+  // Masks of a step's scores (lane row c = 16 kt + 4 gl + e of the step): valid iff (index lists)
+  // its mask bit is set, or (dense) its position j = j0 + 32 t + c is inside the group's rows and
+  // the query row's causal / window range.
+  __device__ __forceinline__ void apply_mask(f32x4 (&s)[2][2], Cur c, int x, const Lane& L) const {
+    const int ln = L.ln;
+    const int nl = ln & 15, gl = ln >> 4;
+    const uint32_t vmask = *reinterpret_cast<const LDS_AS uint32_t*>(sm + kMOff + 4 * (x & 7));
+    const bool dense_mask = !sparse && (a.causal || a.window > 0);
+    const bool need = sparse ? (vmask != ~0u) : (kRows * (c.t + 1) > c.n || dense_mask);
+    if (!need) return;
+    if (sparse) {
+      const uint32_t vm = vmask >> (4 * gl);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = ((vm >> (16 * kt + e)) & 1u) != 0;
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) s[kt][nt][e] = ok ? s[kt][nt][e] : kNegInf;
+        }
+    } else {
+      const int kbase = kRows * c.t + 4 * gl;  // step offset of e = 0, kt = 0
+      const int nrem = c.n - kbase;
+      int hi[2], lo[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const int qrow = mt * 128 + 32 * s + 16 * nt + nl;
-        const int r = min(qrow, a.R - 1);
-        const bf16x8* src = reinterpret_cast<const bf16x8*>(a.q + ((int64_t)g * a.R + r) * DQK + 8 * gl);
+        // the query's position pos = L - Sq + token (token = row / H), relative to the step offset
+        const int rel = c.L - a.Sq + (mt * 128 + 32 * wave + 16 * nt + nl) / a.H - c.j0 - kbase;
+        hi[nt] = a.causal ? rel : (1 << 30);
+        lo[nt] = a.window > 0 ? rel - a.window + 1 : -(1 << 30);
+      }
 #pragma unroll
-        for (int ks = 0; ks < KSQ; ++ks) qr[nt][ks] = src[4 * ks];
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int cc = 16 * kt + e;
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const bool ok = (cc < nrem) & (cc <= hi[nt]) & (cc >= lo[nt]);
+            s[kt][nt][e] = ok ? s[kt][nt][e] : kNegInf;
+          }
+        }
+    }
+  }
+
+  // Softmax of the wave's rows (base 2, lazy reference maximum) in micro-stages of at most two VALU
+  // instructions or one exponential, so the QK^T loop of the next step can run one between each pair
+  // of MFMAs (one wave hides about two VALU instructions under an MFMA): 0-3 row maxima, 4-7 their
+  // reductions over the four lane groups, 8-13 the reference updates, 14-29 the exponentials and
+  // sums (one value each), 30 the row sums.
+  static constexpr int kSoftStages = 31;
+  __device__ __forceinline__ void soft_stage(int st, Soft& f, const f32x4 (&s)[2][2]) const {
+    if (st < 4) {
+      const int nt = st >> 1;
+      if ((st & 1) == 0) {
+        f.part[nt] = fmaxf(fmaxf(s[0][nt][0], s[0][nt][1]), s[0][nt][2]);
+        f.mx[nt] = fmaxf(fmaxf(s[0][nt][3], s[1][nt][0]), s[1][nt][1]);
+      } else {
+        f.part[nt] = fmaxf(fmaxf(s[1][nt][2], s[1][nt][3]), f.part[nt]);
+        f.mx[nt] = fmaxf(f.mx[nt], f.part[nt]);
+      }
+    } else if (st < 6) {
+      const int nt = st - 4;
+      const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(f.mx[nt]), __float_as_uint(f.mx[nt]), false, false);
+      f.mx[nt] = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    } else if (st < 8) {
+      const int nt = st - 6;
+      const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(f.mx[nt]), __float_as_uint(f.mx[nt]), false, false);
+      f.mx[nt] = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    } else if (st < 14) {
+      const int nt = (st - 8) / 3, sub = (st - 8) % 3;
+      if (sub == 0) {
+        f.mnew[nt] = f.mx[nt] * a.scale_log2;  // -inf stays -inf (scale > 0)
+        f.up[nt] = f.mnew[nt] > f.m_ref[nt] + kTau;
+        if constexpr (MAXL) f.m_top[nt] = fmaxf(f.m_top[nt], f.mnew[nt]);
+      } else if (sub == 1) {
+        f.alpha[nt] = f.up[nt] ? __builtin_amdgcn_exp2f(f.m_ref[nt] - f.mnew[nt]) : 1.f;  // m_ref = -inf -> 0
+      } else {
+        f.m_ref[nt] = f.up[nt] ? f.mnew[nt] : f.m_ref[nt];
+        f.l_acc[nt] *= f.alpha[nt];
+        f.mu[nt] = (f.m_ref[nt] == kNegInf) ? 0.f : f.m_ref[nt];
+        f.lsum[nt] = 0.f;
+      }
+    } else if (st < 30) {
+      const int v = st - 14, nt = v & 1, kt = (v >> 1) >> 2, e = (v >> 1) & 3;
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][nt][e], a.scale_log2, -f.mu[nt]));
+      f.lsum[nt] += pv;
+      f.pf[nt][kt * 4 + e] = (__bf16)pv;
+    } else if (st == 30) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) f.l_acc[nt] += f.lsum[nt];
+    }
+  }
+  __device__ __forceinline__ void soft_reset(Soft& f) const {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f.m_ref[nt] = kNegInf;
+      f.l_acc[nt] = 0.f;
+      f.m_top[nt] = kNegInf;
+    }
+  }
+
+  // Side work of MFMA slot sl of an iteration (0 .. 4 KS - 1: QK^T, then 64 PV slots): the
+  // transfers of the bundle being sent, one every kDmaGap slots, so the CU's LDS-DMA unit (about one
+  // 1 KB transfer per 46 cycles) sees an even stream instead of bursts.
+  static constexpr int kSlots = 4 * KS + 64;
+  static constexpr int kDmaGap = kSlots / kNb;
+  __device__ __forceinline__ int dma_part(int i) const { return (i < 8 || HAS_B) ? i : i + 1; }
+  template <bool SEND>
+  __device__ __forceinline__ void side_dma(int sl, int y, Cur cp, Cur cx, uint64_t& next, const DAddr& d,
+                                           const Lane& L) const {
+    if constexpr (SEND) {
+      if (sl % kDmaGap == 1 && sl / kDmaGap < kNb) send_part(dma_part(sl / kDmaGap), y, cp, cx, next, d, L);
+    }
+  }
+
+  // S^T = K Q^T of step x (slot x % 4), with the softmax micro-stages of the previous step (SOFT)
+  // and the first transfers of bundle y (SEND) between the MFMAs.
+  template <bool SOFT, bool SEND>
+  __device__ __forceinline__ void qk(f32x4 (&sacc)[2][2], const bf16x8 (&qr)[2][KS], int x, Soft& f,
+                                    const f32x4 (&sold)[2][2], int y, Cur cp, Cur cx, const DAddr& d,
+                                    uint64_t& next, const Lane& L) const {
+    const int nl = L.ln & 15, gl = L.ln >> 4;
+    const uint32_t sa = (uint32_t)(x & (NS - 1)) * kSlot;
+    const uint32_t sb = sa + kSlotA;
+    const uint32_t kaddr = sa + nl * kRowStrideA + 16 * gl;
+    auto k_op = [&](int kt, int ks) -> bf16x8 {
+      if (ks < 16) return lds_read_b128(sm, kaddr + 16 * kt * kRowStrideA + 64 * ks);
+      const int row = 16 * kt + nl;
+      const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
+      return lds_read_b128(sm, sb + row * 128 + 16 * c);
+    };
+    constexpr int D = 3;  // operand steps in flight
+    bf16x8 ka[D][2];
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) ka[i][kt] = k_op(kt, i);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int kt = m >> 1, nt = m & 1, sl = 4 * ks + m;
+        if (ks + D - 1 < KS && nt == 0) ka[(ks + D - 1) % D][kt] = k_op(kt, ks + D - 1);
+        if (ks == 0) mfma_s0(sacc[kt][nt], ka[ks % D][kt], qr[nt][ks]);
+        else mfma_s(sacc[kt][nt], ka[ks % D][kt], qr[nt][ks]);
+        if constexpr (SOFT) {  // stages spread evenly over the 4 KS slots
+#pragma unroll
+          for (int st = 0; st < kSoftStages; ++st)
+            if ((st * 4 * KS) / kSoftStages == sl) soft_stage(st, f, sold);
+        }
+        side_dma<SEND>(sl, y, cp, cx, next, d, L);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if constexpr (HAS_B) {
-      // eight rows of 128 bytes per LDS-DMA instruction; lane l brings chunk (l & 7) ^ swz(row) of
-      // row (l >> 3), so the LDS copy is swizzled like the RoPE tails of the KV rows
+    mfma_drain4(sacc[0][0], sacc[0][1], sacc[1][0], sacc[1][1]);
+  }
+
+  // O^T (+)= V^T P^T of step x over all 512 output columns (FIRST: zero accumulator), with the rest
+  // of bundle y's transfers between the MFMAs (SEND).
+  template <bool FIRST, bool PREP, bool SEND>
+  __device__ __forceinline__ void pv(f32x4 (&o)[32][2], const bf16x8 (&pf)[2], int x, Cur c, int y, Cur cp,
+                                    Cur cx, const DAddr& d, uint64_t& next, const Lane& L) const {
+    const int nl = L.ln & 15, gl = L.ln >> 4;
+    const uint32_t sa = (uint32_t)(x & (NS - 1)) * kSlot;
+    const uint32_t vbase = sa + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (nl & 3);
+    auto v_op = [&](int ct) -> bf16x8 {
+      const uint32_t ad = vbase + 32 * ct;
+      const bf16x4 v0 = lds_read_tr(sm, ad);
+      const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    constexpr int VD = 4;
+    bf16x8 va[VD];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int row = 32 * s + 8 * k + (lane >> 3);  // row of the tile
-        const int r = min(mt * 128 + row, a.R - 1);
-        const uint16_t* src = a.q + ((int64_t)g * a.R + r) * DQK + 512 + 8 * ((lane & 7) ^ swz_b(row));
-        dma_x4(src, lds_addr(sm + kQrOff + (32 * s + 8 * k) * 128));
+    for (int i = 0; i < VD - 1; ++i) va[i] = v_op(i);
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct) {
+      if (ct + VD - 1 < 32) va[(ct + VD - 1) % VD] = v_op(ct + VD - 1);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int sl = 4 * KS + 2 * ct + nt;
+        if (FIRST) mfma_o0(o[ct][nt], va[ct % VD], pf[nt]);
+        else mfma_o(o[ct][nt], va[ct % VD], pf[nt]);
+        side_dma<SEND>(sl, y, cp, cx, next, d, L);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+
+  // rescale O^T where a row's reference maximum moved (rare once a split is under way)
+  __device__ __forceinline__ void rescale(f32x4 (&o)[32][2], const Soft& f) const {
+    if (!__any(f.up[0] | f.up[1])) return;
+    mfma_drain_acc(o);
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) o[ct][nt] *= f.alpha[nt];
+      asm volatile("" : "+a"(o[ct][0]), "+a"(o[ct][1]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // One pipeline iteration k: QK^T of step k (cursor cq), softmax and PV of step k - 1 (cursor cs),
+  // bundle k + 2 sent (its page and index steps: cp, cx), bundle k + 3 prepared (cursor cb; PREP);
+  // EPI: step k - 1 ends its split, whose rows are then normalised and stored. A split boundary
+  // splits iteration k in two: its PV part (EPI, no PREP) ends the old split, its QK part (no PV)
+  // starts the new one once that split's Q^T is loaded.
+  template <bool HAS_QK, bool HAS_PV, bool EPI, bool PREP>
+  __device__ __forceinline__ void iteration(int k, bf16x8 (&qr)[2][KS], f32x4 (&o)[32][2], f32x4 (&sold)[2][2],
+                                            Soft& f, Cur& cq, Cur& cs, Cur& cb, Cur& cp, Cur& cx, DRows& dn,
+                                            int cbase) {
+    if constexpr (HAS_QK) wait_landed();
+    lds_barrier();  // rows of step k visible; every wave is done with steps k - 2 (PV) and k - 1 (QK)
+    DAddr da;
+    if constexpr (HAS_QK && !SPARSE) da = dense_addr(dn);  // bundle k + 2 (entries loaded a step ago)
+    Lane L;
+    L.ln = lane_id();
+    L.v16 = 16u * (uint32_t)L.ln;
+    if constexpr (HAS_PV) {
+      if (cs.t == cs.q0) soft_reset(f);  // the softmax starts a new split
+      apply_mask(sold, cs, k - 1, L);
+    }
+    const int ysend = cb.y - 1;  // bundle k + 2
+    uint64_t next = 0;
+    if constexpr (HAS_QK && SPARSE) next = rb_read(0);
+    f32x4 snew[2][2];
+    if constexpr (HAS_QK) {
+      qk<HAS_PV, true>(snew, qr, k, f, sold, ysend, cp, cx, da, next, L);
+    } else {
+#pragma unroll
+      for (int st = 0; st < kSoftStages; ++st) soft_stage(st, f, sold);
+    }
+    if constexpr (HAS_PV) {
+      const bool first = cs.t == cs.q0;
+      if (!first) rescale(o, f);
+      asm volatile("s_nop 4" ::: "memory");  // P^T written by VALU, O^T rescaled: wait states
+      if (first) pv<true, PREP, HAS_QK>(o, f.pf, k - 1, cb, ysend, cp, cx, da, next, L);
+      else pv<false, PREP, HAS_QK>(o, f.pf, k - 1, cb, ysend, cp, cx, da, next, L);
+      // index lists: the next bundle's addresses, once this bundle's transfers have read the table
+      if constexpr (PREP && SPARSE) prepare(cb, L);
+      if constexpr (EPI) {  // the split's last step: normalise and store its rows
+        lds_barrier();  // every wave is done reading slot k - 1: it stages the epilogue
+        epilogue(cbase + cs.ci, cs.g, desc(cs.ci, D_NSPLIT), (uint32_t)((k - 1) & (NS - 1)) * kSlot, o, f, L);
+      }
+    } else {
+      // no PV: the transfers placed among the PV MFMAs go out here
+#pragma unroll
+      for (int sl = 4 * KS; sl < kSlots; ++sl) side_dma<HAS_QK>(sl, ysend, cp, cx, next, da, L);
+      if constexpr (PREP && SPARSE) prepare(cb, L);
+    }
+    if constexpr (PREP) {
+      if constexpr (!SPARSE) dn = dense_rows(cb);
+      cb = cur_next(cb);
+      if constexpr (SPARSE) {
+        cp = cur_next(cp);
+        cx = cur_next(cx);
+      }
+    }
+    if constexpr (HAS_QK) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) sold[kt][nt] = snew[kt][nt];
+      cs = cq;
+      cq = cur_next(cq);
+    }
+  }
+
+  __device__ void run_chunk(int cb0) {
+    const Cur c0 = cur_begin();
+    Cur cb = c0, cp = c0, cx = c0;  // next bundle, block-table and index steps
+    // ---- prologue: Q^T of the first split, index and block-table entries, bundles 0-1 --------
+    bf16x8 qr[2][KS];
+    load_q(qr, c0.g);
+    if (sparse) {
+#pragma unroll 1
+      for (int i = 0; i < 6; ++i) {
+        dma_dword(idx_src(cx), ix_slot(cx.y));
+        cx = cur_next(cx);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    if (sparse) {
+#pragma unroll 1
+      for (int i = 0; i < 3; ++i) {
+        dma_dword(page_src(cp), pg_slot(cp.y));
+        cp = cur_next(cp);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) asm volatile("" : "+v"(qr[nt][ks]));
-    f32x4 o[8][2];  // O^T of the own rows: [output column tile][row tile]; the first step's
-                    // MFMAs write it with a zero accumulator
-    const bool dense_mask = !sparse && (a.causal || a.window > 0);
-    float m_ref[2] = {kNegInf, kNegInf}, l_acc[2] = {0.f, 0.f};
-    float m_top[2] = {kNegInf, kNegInf};  // MAXL: the rows' true maxima (m_ref trails them by up to kTau)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q RoPE part in LDS
-    lds_barrier();  // B_q0: counters cleared, Q RoPE part written
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qr[nt][ks]));  // Q^T has landed
+    DRows dn;
+    Lane L0;
+    L0.ln = lane_id();
+    L0.v16 = 16u * (uint32_t)L0.ln;
+#pragma unroll 1
+    for (int i = 0; i < 2; ++i) {
+      DAddr d0;
+      if constexpr (SPARSE) prepare(cb, L0);
+      else d0 = dense_addr(dense_rows(cb));
+      send_all(cb.y, cp, cx, d0, L0);
+      cb = cur_next(cb);
+      if constexpr (SPARSE) {
+        cp = cur_next(cp);
+        cx = cur_next(cx);
+      }
+    }
+    if constexpr (SPARSE) prepare(cb, L0);  // bundle 2
+    else dn = dense_rows(cb);
+    cb = cur_next(cb);
 
-    for (int t = q0; t < qend; ++t) {
-      const int ln = opaque_lane();
-      const int nl = ln & 15, gl = ln >> 4;
-      const int k = t - q0;  // step index within the split
-      wait4(kCLanded, k + 1);  // rows of step t in LDS
-      const uint32_t sa = slot_of(t);
-      const uint32_t sb = sa + kSlotA;
-      bf16x8 pf[2];
-      float alpha[2] = {1.f, 1.f};
-      bool any_up = false;
-      {
-        // ---- S^T = K Q^T: 32 step rows x the wave's 32 rows ---------------------------------
-        const uint32_t kaddr = sa + nl * kRowStrideA + 16 * gl;
-        auto k_op = [&](int kt, int ks) -> bf16x8 {
-          if (ks < 16) return lds_read_b128(sm, kaddr + 16 * kt * kRowStrideA + 64 * ks);
-          const int row = 16 * kt + nl;
-          const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
-          return lds_read_b128(sm, sb + row * 128 + 16 * c);
-        };
-        auto q_rope = [&](int nt, int ks) -> bf16x8 {  // RoPE k steps of Q^T, from LDS
-          const int row = 32 * s + 16 * nt + nl;
-          const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
-          return lds_read_b128(sm, kQrOff + row * 128 + 16 * c);
-        };
-        constexpr int D = 2;  // operand steps in flight
-        bf16x8 ka[D][2];
+    f32x4 o[32][2];  // O^T: [output column tile][row tile], in accumulation registers
+    f32x4 sold[2][2];
+    Soft f;
+    soft_reset(f);
+    Cur cq = c0, cs = c0;
+    // One pipelined loop per split. A split's Q^T is loaded between loops, so no loop holds a load
+    // whose wait the compiler would place among the MFMAs (such a wait would also hold for the row
+    // transfers in flight).
+    int k = 0;
+#pragma unroll 1
+    for (int ci = 0; ci < nc; ++ci) {
+      if (ci > 0) {
+        load_q(qr, cq.g);  // cq: the split's first step
 #pragma unroll
-        for (int i = 0; i < D - 1; ++i)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) ka[i][kt] = k_op(kt, i);
-        f32x4 sacc[2][2];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (ks + D - 1 < KS) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) ka[(ks + D - 1) % D][kt] = k_op(kt, ks + D - 1);
-          }
-          if (ks < KSQ) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int nt = 0; nt < 2; ++nt) {
-                if (ks == 0) mfma_vv0(sacc[kt][nt], ka[ks % D][kt], qr[nt][ks]);
-                else mfma_vv(sacc[kt][nt], ka[ks % D][kt], qr[nt][ks]);
-              }
-          } else {
-            const bf16x8 qa = q_rope(0, ks), qb = q_rope(1, ks);
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-              mfma_vv(sacc[kt][0], ka[ks % D][kt], qa);
-              mfma_vv(sacc[kt][1], ka[ks % D][kt], qb);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);  // keep the operand loads D - 1 steps ahead only
-        }
-        mfma_drain4(sacc[0][0], sacc[0][1], sacc[1][0], sacc[1][1]);
+          for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qr[nt][ks]));  // Q^T has landed
+      }
+      const int kend = k + (cq.qend - cq.q0);
+      iteration<true, false, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0);
+#pragma unroll 1
+      for (++k; k < kend; ++k) iteration<true, true, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0);
+      iteration<false, true, true, false>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the zero-row bundles past the end
+  }
 
-        // ---- masks ---------------------------------------------------------------------------
-        const bool tail = 32 * (t + 1) > n;
-        const uint32_t vmask = *reinterpret_cast<const LDS_AS uint32_t*>(sm + kMOff + 4 * (t & 3));
-        const bool need_mask = sparse ? (vmask != ~0u) : (tail || dense_mask);
-        if (need_mask) {
-          // step row c = 16 kt + e of the lane's group: valid iff (sparse) its mask bit is set, or
-          // (dense) its position j = j0 + 32 t + 4 gl + c is inside the group's rows and the query
-          // row's causal / window range; every test is a register against an immediate
-          if (sparse) {
-            const uint32_t vm = vmask >> (4 * gl);
+  // Normalise the wave's 32 rows, stage them through slot LDS `stage` (16 rows x 256 columns at a
+  // time) and store them as whole 128-byte lines, with their LSE; a group of one split gets its
+  // final outputs (sink folded in), others partials.
+  __device__ __forceinline__ void epilogue(int split, int g, int nsplit, uint32_t stage, f32x4 (&o)[32][2],
+                                           const Soft& f, const Lane& L) const {
+    mfma_drain_acc(o);
+    const bool final_out = (nsplit == 1);
+    const uint32_t wst = stage + wave * 16 * kStageRow;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const bool ok = ((vm >> (16 * kt + e)) & 1u) != 0;
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) sacc[kt][nt][e] = ok ? sacc[kt][nt][e] : kNegInf;
-              }
-          } else {
-            const int kbase = 32 * t + 4 * gl;        // step offset of c = 0
-            const int nrem = n - kbase;                // c < nrem
-            int hi[2], lo[2];
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-              // the query's position pos = L - Sq + token (token = row / H), in units of c
-              const int qrow = mt * 128 + 32 * s + 16 * nt + nl;
-              const int rel = L - a.Sq + qrow / a.H - j0 - kbase;
-              hi[nt] = a.causal ? rel : (1 << 30);
-              lo[nt] = a.window > 0 ? rel - a.window + 1 : -(1 << 30);
-            }
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int c = 16 * kt + e;
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                  const bool ok = (c < nrem) & (c <= hi[nt]) & (c >= lo[nt]);
-                  sacc[kt][nt][e] = ok ? sacc[kt][nt][e] : kNegInf;
-                }
-              }
-          }
-        }
-
-        // ---- softmax of the wave's rows (base 2, lazy reference maximum) ---------------------
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          float mx = kNegInf;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kt][nt][e]);
-          mx = rows_max(mx);
-          const float mnew = mx * a.scale_log2;  // -inf stays -inf (scale > 0)
-          if constexpr (MAXL) m_top[nt] = fmaxf(m_top[nt], mnew);
-          if (mnew > m_ref[nt] + kTau) {
-            alpha[nt] = __builtin_amdgcn_exp2f(m_ref[nt] - mnew);  // m_ref = -inf -> 0
-            m_ref[nt] = mnew;
-            l_acc[nt] *= alpha[nt];
-            any_up = true;
-          }
-          const float mu = (m_ref[nt] == kNegInf) ? 0.f : m_ref[nt];
-          float lsum = 0.f;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][nt][e], a.scale_log2, -mu));
-              lsum += pv;
-              pf[nt][kt * 4 + e] = (__bf16)pv;
-            }
-          l_acc[nt] += lsum;
+    for (int nt = 0; nt < 2; ++nt) {
+      const int nl = L.ln & 15, gl = L.ln >> 4;
+      const float lt = rows_sum(f.l_acc[nt]);
+      const int r = mt * 128 + 32 * wave + 16 * nt + nl;
+      float lse_nat, scale;
+      row_norm(g, min(r, a.R - 1), f.m_ref[nt], lt, final_out, &lse_nat, &scale);
+      if (gl == 0 && r < a.R) {
+        st_global_b32(final_out ? a.lse + lse_index(g, r) : a.part_lse + (int64_t)split * a.R + r, lse_nat);
+        if constexpr (MAXL) {  // natural-log units of the scaled scores
+          const float ml = f.m_top[nt] * 0.69314718055994530942f;
+          st_global_b32(final_out ? a.max_logits + lse_index(g, r) : a.part_max + (int64_t)split * a.R + r, ml);
         }
       }
-      // ---- publish P^T of step t and its rescale factors into buffer t & 1, once the value waves
-      // hold P^T of step t - 2 (the buffer's previous contents) ---------------------------------
-      const uint32_t pb = (uint32_t)(t & 1);
-      const bool wave_up = __any(any_up);
-      wait4(kCPConsumed, k - 1);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        *reinterpret_cast<LDS_AS bf16x8*>(sm + kPOff + pb * 8192 + ((2 * s + nt) * 64 + ln) * 16) = pf[nt];
-        if (gl == 0) *reinterpret_cast<LDS_AS float*>(sm + kAOff + pb * 512 + 4 * (32 * s + 16 * nt + nl)) = alpha[nt];
-      }
-      if (ln == 0) *reinterpret_cast<LDS_AS int*>(sm + kFOff + pb * 16 + 4 * s) = wave_up ? 1 : 0;
-      signal(kCPReady, s, k + 1);
-      // ---- own rows: rescale, then O^T += V^T P^T for columns [128s, 128s + 128) --------------
-      const bool first = (k == 0);
-      if (wave_up && !first) {
-        mfma_drain_v(o);
+      for (int h = 0; h < 2; ++h) {
+        // lane (nl, gl): columns 16 ct + 4 gl .. + 3 of row nl, ct in [16h, 16h + 16)
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) o[ct][nt] *= alpha[nt];
-          asm volatile("" : "+v"(o[ct][0]), "+v"(o[ct][1]));
+        for (int c = 0; c < 16; ++c) {
+          const f32x4 v = acc_read(o[16 * h + c][nt]) * scale;
+          const u32x2 w = {(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                           (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
+          *reinterpret_cast<LDS_AS u32x2*>(sm + wst + nl * kStageRow + 32 * c + 8 * gl) = w;
           __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      const uint32_t vbase = sa + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (ln & 3) + 2 * (128 * s);
-      auto v_op = [&](int ct) -> bf16x8 {
-        const uint32_t ad = vbase + 32 * ct;
-        const bf16x4 v0 = lds_read_tr(sm, ad);
-        const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
-        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      bf16x8 va[8];  // every V^T operand of the step in flight at once (QK^T's registers are free)
+        // lane l: 16 bytes at column 8 (l & 31) of staged row 2 i + (l >> 5)
+        const int ln = L.ln;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) va[ct] = v_op(ct);
-      asm volatile("s_nop 4" ::: "memory");  // P^T written by VALU, O^T rescaled: wait states
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        if (first) {
-          mfma_vv0(o[ct][0], va[ct], pf[0]);
-          mfma_vv0(o[ct][1], va[ct], pf[1]);
-        } else {
-          mfma_vv(o[ct][0], va[ct], pf[0]);
-          mfma_vv(o[ct][1], va[ct], pf[1]);
-        }
-      }
-      signal(kCReleased, s, k + 1);  // rows of step t read for the last time by this wave
-    }
-    mfma_drain_v(o);
-    const int ln = opaque_lane();
-    const int nl = ln & 15, gl = ln >> 4;
-    // ---- row statistics for the value waves ----------------------------------------------------
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float lt = rows_sum(l_acc[nt]);
-      const int hrow = 32 * s + 16 * nt + nl;
-      if (gl == 0) {
-        *reinterpret_cast<LDS_AS float*>(sm + kLOff + 4 * hrow) = lt;
-        *reinterpret_cast<LDS_AS float*>(sm + kLOff + 512 + 4 * hrow) = m_ref[nt];
-        const int r = mt * 128 + hrow;
-        if (MAXL && r < a.R) {  // natural-log units of the scaled scores
-          const float ml = m_top[nt] * 0.69314718055994530942f;
-          if (nsplit == 1) a.max_logits[lse_index(r)] = ml;
-          else a.part_max[(int64_t)cur_split * a.R + r] = ml;
-        }
-      }
-      l_acc[nt] = lt;
-    }
-    lds_barrier();  // E1: statistics published; every transfer has landed
-    // ---- own rows: normalise into the staging rows, LSE -----------------------------------------
-    const bool final_out = (nsplit == 1);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int hrow = 32 * s + 16 * nt + nl;
-      const int r = mt * 128 + hrow;
-      float lse_nat, scale;
-      row_norm(min(r, a.R - 1), m_ref[nt], l_acc[nt], final_out, &lse_nat, &scale);
-      const uint32_t row_at = hrow * kStageRow + 2 * (128 * s + 4 * gl);
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const f32x4 v = o[ct][nt] * scale;
-        const u32x2 w = {(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
-                         (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
-        *reinterpret_cast<LDS_AS u32x2*>(sm + row_at + 32 * ct) = w;
-      }
-      if (gl == 0 && r < a.R) {
-        if (final_out) a.lse[lse_index(r)] = lse_nat;
-        else a.part_lse[(int64_t)cur_split * a.R + r] = lse_nat;
-      }
-    }
-    lds_barrier();  // E2: output rows staged
-    store_rows(mt);
-    lds_barrier();  // E3: staging area and slots reused by the next split
-  }
-
-  // Output rows of the tile leave LDS as whole 1 KB rows: wave w stores rows [16w, 16w + 16).
-  __device__ __forceinline__ void store_rows(int mt) {
-    const int s = cur_split;
-    const bool final_out = (nsplit == 1);
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int hrow = 16 * wave + rr;
-      const int r = mt * 128 + hrow;
-      if (r < a.R) {
-        const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(sm + hrow * kStageRow + 16 * lane);
-        uint16_t* dst = final_out ? a.out + ((int64_t)g * a.R + r) * kDv : a.part_o + ((int64_t)s * a.R + r) * kDv;
-        *reinterpret_cast<u32x4*>(dst + 8 * lane) = v;
-      }
-    }
-  }
-
-  // ===== value waves ===========================================================================
-  __device__ void value_split(int mt) {
-    const int vw = wave - 4;  // the SIMD's score wave index
-    const bool sparse = a.topk > 0;
-    __builtin_assume(vw >= 0 && vw < 4);
-    f32x4 o[8][6];  // O^T of the other 96 rows: [output column tile][row tile jj]; the first
-                    // accumulated step writes it with a zero accumulator
-    // row tile jj of this wave = row tile j of the workgroup, skipping the score wave's own two
-    auto tile_of = [&](int jj) -> int { return jj + (jj >= 2 * vw ? 2 : 0); };
-
-    // ---- prologue: row entries of the first steps, bundles q0 .. q0 + 2 ------------------------
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // rings free
-    if (wave == 4 && lane < 20) *reinterpret_cast<LDS_AS int*>(sm + kCOff + 4 * lane) = 0;  // counters
-    if (sparse) {
-#pragma unroll
-      for (int i = 0; i < 6; ++i) idx_fetch(q0 + i);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-#pragma unroll
-    for (int i = 0; i < 3; ++i) page_fetch(q0 + i);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    issue(q0, prep(q0));
-    issue(q0 + 1, prep(q0 + 1));
-    issue(q0 + 2, prep(q0 + 2));
-    lds_barrier();  // B_q0: counters cleared
-    // bundle q0 landed (bundles q0 + 1, q0 + 2 may be in flight)
-    if (sparse) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * (kDmaOps + 2)) : "memory");
-    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * (kDmaOps + 1)) : "memory");
-    signal(kCLanded, vw, 1);
-
-    for (int t = q0; t < qend; ++t) {
-      const int k = t - q0;
-      // bundle t + 1 landed (bundle t + 2 may be in flight): its rows are the score waves' next
-      if (sparse) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaOps + 2) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaOps + 1) : "memory");
-      signal(kCLanded, vw, k + 2);
-      const Prep next = prep(t + 3);  // addresses of bundle t + 3 (their LDS reads overlap the wait)
-      // ---- step t: P^T, flags and rescale factors once the score waves have published them -----
-      wait4(kCPReady, k + 1);
-      const int ln = opaque_lane();
-      const int nl = ln & 15, gl = ln >> 4;
-      const uint32_t pbo = (uint32_t)(t & 1);
-      const LDS_AS int* fl = reinterpret_cast<const LDS_AS int*>(sm + kFOff + pbo * 16);
-      const int f0 = fl[0], f1 = fl[1], f2 = fl[2], f3 = fl[3];
-      const int fmask = ((f0 ? 1 : 0) | (f1 ? 2 : 0) | (f2 ? 4 : 0) | (f3 ? 8 : 0)) & ~(1 << vw);
-      const bool first = (k == 0);
-      bf16x8 pb[6];
-#pragma unroll
-      for (int jj = 0; jj < 6; ++jj)
-        pb[jj] = *reinterpret_cast<const LDS_AS bf16x8*>(sm + kPOff + pbo * 8192 + (tile_of(jj) * 64 + ln) * 16);
-      float al[6];
-      if (fmask && !first) {
-#pragma unroll
-        for (int jj = 0; jj < 6; ++jj)
-          al[jj] = *reinterpret_cast<const LDS_AS float*>(sm + kAOff + pbo * 512 + 4 * (16 * tile_of(jj) + nl));
-      }
-      signal(kCPConsumed, vw, k + 1);  // P^T buffer t & 1 may be overwritten (with step t + 2)
-      if (fmask && !first) {
-        // only the row tiles whose score wave moved its reference maximum
-        mfma_drain_v(o);
-#pragma unroll
-        for (int jj = 0; jj < 6; ++jj) {
-          if (!((fmask >> (tile_of(jj) >> 1)) & 1)) continue;
-#pragma unroll
-          for (int ct = 0; ct < 8; ++ct) {
-            o[ct][jj] *= al[jj];
-            asm volatile("" : "+v"(o[ct][jj]));
-            __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 8; ++i) {
+          const int row = 2 * i + (ln >> 5);
+          const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(sm + wst + row * kStageRow + 16 * (ln & 31));
+          const int rr = mt * 128 + 32 * wave + 16 * nt + row;
+          if (rr < a.R) {
+            uint16_t* dst = final_out ? a.out + ((int64_t)g * a.R + rr) * kDv : a.part_o + ((int64_t)split * a.R + rr) * kDv;
+            st_global_b128(dst + 256 * h + 8 * (ln & 31), v);
           }
         }
-        asm volatile("s_nop 4" ::: "memory");
-      }
-      const uint32_t vbase = slot_of(t) + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (ln & 3) + 2 * (128 * vw);
-      auto v_op = [&](int ct) -> bf16x8 {
-        const uint32_t ad = vbase + 32 * ct;
-        const bf16x4 v0 = lds_read_tr(sm, ad);
-        const bf16x4 v1 = lds_read_tr(sm, ad + 16 * kRowStrideA);
-        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      constexpr int VD = 3;
-      bf16x8 va[VD];
-#pragma unroll
-      for (int i = 0; i < VD - 1; ++i) va[i] = v_op(i);
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        if (ct + VD - 1 < 8) va[(ct + VD - 1) % VD] = v_op(ct + VD - 1);
-        if (first) {
-#pragma unroll
-          for (int jj = 0; jj < 6; ++jj) mfma_vv0(o[ct][jj], va[ct % VD], pb[jj]);
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < 6; ++jj) mfma_vv(o[ct][jj], va[ct % VD], pb[jj]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      signal(kCReleased, 4 + vw, k + 1);  // rows of step t read for the last time by this wave
-      // ---- bundle t + 3 into the slot of step t, once all eight waves have released it ---------
-      wait8(kCReleased, k + 1);
-      issue(t + 3, next);
-    }
-    // the last bundles (zero-row reads) must land before the slots are reused
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    mfma_drain_v(o);
-    lds_barrier();  // E1: score waves' statistics published
-
-    // ---- epilogue: normalise the 96 rows x 128 columns into the staging rows ------------------
-    const int ln = opaque_lane();
-    const int nl = ln & 15, gl = ln >> 4;
-    const bool final_out = (nsplit == 1);
-#pragma unroll
-    for (int jj = 0; jj < 6; ++jj) {
-      const int hrow = 16 * tile_of(jj) + nl;
-      const int r = mt * 128 + hrow;
-      const float lt = *reinterpret_cast<const LDS_AS float*>(sm + kLOff + 4 * hrow);
-      const float m2 = *reinterpret_cast<const LDS_AS float*>(sm + kLOff + 512 + 4 * hrow);
-      float lse_nat, scale;
-      row_norm(min(r, a.R - 1), m2, lt, final_out, &lse_nat, &scale);
-      const uint32_t row_at = hrow * kStageRow + 2 * (128 * vw + 4 * gl);
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const f32x4 v = o[ct][jj] * scale;
-        const u32x2 w = {(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
-                         (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
-        *reinterpret_cast<LDS_AS u32x2*>(sm + row_at + 32 * ct) = w;
       }
     }
-    lds_barrier();  // E2: output rows staged
-    store_rows(mt);
-    lds_barrier();  // E3: staging area and slots reused by the next split
   }
 
   // LSE (natural log) and output scale of a row; the sink is folded in for final outputs.
-  __device__ __forceinline__ void row_norm(int r, float m2, float l, bool final_out, float* lse_nat,
-                                           float* scale) const {
+  __device__ __forceinline__ void row_norm(int g, int r, float m2, float l, bool final_out,
+                                           float* lse_nat, float* scale) const {
     const float kLn2 = 0.69314718055994530942f;
+    const float* sk_p = (final_out && a.sink != nullptr) ? a.sink + (sparse ? r : r % a.H) : nullptr;
     if (l > 0.f) {
       float lse = (m2 + __log2f(l)) * kLn2;
       float sc = 1.f / l;
-      if (final_out && a.sink != nullptr) {
-        const float sk = a.sink[(a.topk > 0) ? r : r % a.H];
+      if (sk_p != nullptr) {
+        const float sk = *sk_p;
         const float mx = fmaxf(lse, sk);
         const float lse2 = mx + __logf(__expf(lse - mx) + __expf(sk - mx));
         sc *= __expf(lse - lse2);
@@ -1950,12 +2053,12 @@ struct Spec128 {
       *scale = sc;
     } else {
       *scale = 0.f;
-      *lse_nat = (final_out && a.sink != nullptr) ? a.sink[(a.topk > 0) ? r : r % a.H] : kNegInf;
+      *lse_nat = (sk_p != nullptr) ? *sk_p : kNegInf;
     }
   }
-  __device__ __forceinline__ int64_t lse_index(int r) const {
+  __device__ __forceinline__ int64_t lse_index(int g, int r) const {
     int bb, t, h;
-    if (a.topk > 0) {
+    if (sparse) {
       bb = g / a.Sq;
       t = g % a.Sq;
       h = r;
@@ -1966,7 +2069,43 @@ struct Spec128 {
     }
     return ((int64_t)bb * a.H + h) * a.Sq + t;
   }
+
+  __device__ void run_unit(int s0, int s1) {
+#pragma unroll 1
+    for (int cb = s0; cb < s1; cb += kChunk) {
+      nc = min(kChunk, s1 - cb);
+      lds_barrier();  // every wave is done with the previous chunk's table and slots
+      build_table(cb);
+      lds_barrier();
+      T = 0;
+#pragma unroll 1
+      for (int ci = 0; ci < nc; ++ci) T += desc(ci, D_QEND) - desc(ci, D_Q0);
+      run_chunk(cb);
+    }
+  }
 };
+
+// Workgroup b -> (unit, row tile) for the 128-row kernel: workgroups are dealt to the 8 XCDs
+// round-robin; XCD x takes units [x * per, (x + 1) * per), all row tiles of a unit together, so the
+// splits of one request (consecutive units) share one L2 for their Q rows and block-table entries.
+__device__ __forceinline__ void unit_tile_blocked(int bid, int m_tiles, int per, int* unit, int* mt) {
+  const int x = bid & 7, q = bid >> 3;
+  *mt = q % m_tiles;
+  *unit = x * per + q / m_tiles;
+}
+
+template <int DQK, bool MAXL, bool SPARSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_tile128_kernel(DecodeArgs a, int per) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Tile128<DQK, MAXL, SPARSE>::LDS];
+  int unit, mt;
+  unit_tile_blocked(blockIdx.x, a.m_tiles, per, &unit, &mt);
+  if (unit >= a.U || !plan_matches(a.plan, a.G, a.U, a.R)) return;
+  const int s0 = a.plan[a.unit_ptr_off + unit];
+  const int s1 = a.plan[a.unit_ptr_off + unit + 1];
+  Tile128<DQK, MAXL, SPARSE> d(a, (lds_ptr)lds, mt);
+  d.run_unit(s0, s1);
+}
 
 // Workgroup b -> (unit, row tile): all row tiles of a unit land on the same XCD (workgroups are
 // dealt to the 8 XCDs round-robin), so the second reader of a KV block finds it in that L2.
@@ -1996,39 +2135,6 @@ void decode_spec64_kernel(DecodeArgs a) {
     for (int s = s0; s < s1; ++s) {
       d.load_split(s);
       d.value_split(s, mt);
-    }
-  }
-}
-
-// Workgroup b -> (unit, row tile) for the 128-row kernel: workgroups are dealt to the 8 XCDs
-// round-robin; XCD x takes units [x * per, (x + 1) * per), all row tiles of a unit together, so the
-// splits of one request (consecutive units) share one L2 for their Q rows and block-table entries.
-__device__ __forceinline__ void unit_tile_blocked(int bid, int m_tiles, int per, int* unit, int* mt) {
-  const int x = bid & 7, q = bid >> 3;
-  *mt = q % m_tiles;
-  *unit = x * per + q / m_tiles;
-}
-
-template <int DQK, bool MAXL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_spec128_kernel(DecodeArgs a, int per) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[Spec128<DQK, MAXL>::LDS];
-  const lds_ptr base = (lds_ptr)lds;
-  int unit, mt;
-  unit_tile_blocked(blockIdx.x, a.m_tiles, per, &unit, &mt);
-  if (unit >= a.U || !plan_matches(a.plan, a.G, a.U, a.R)) return;
-  const int s0 = a.plan[a.unit_ptr_off + unit];
-  const int s1 = a.plan[a.unit_ptr_off + unit + 1];
-  Spec128<DQK, MAXL> d(a, base);
-  if (d.wave < 4) {
-    for (int s = s0; s < s1; ++s) {
-      d.load_split(s);
-      d.score_split(mt);
-    }
-  } else {
-    for (int s = s0; s < s1; ++s) {
-      d.load_split(s);
-      d.value_split(mt);
     }
   }
 }
@@ -2068,22 +2174,26 @@ hipError_t launch_spec64(DecodeArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DQK, bool SPARSE>
+hipError_t launch_tile128_t(const DecodeArgs& a, int per, int64_t grid, hipStream_t s) {
+  if (a.max_logits != nullptr)
+    hipLaunchKernelGGL((decode_tile128_kernel<DQK, true, SPARSE>), dim3((unsigned)grid), dim3(256), 0, s, a, per);
+  else
+    hipLaunchKernelGGL((decode_tile128_kernel<DQK, false, SPARSE>), dim3((unsigned)grid), dim3(256), 0, s, a, per);
+  return hipGetLastError();
+}
 template <int DQK>
-hipError_t launch_spec128(DecodeArgs a, hipStream_t s) {
+hipError_t launch_tile128(DecodeArgs a, hipStream_t s) {
   a.m_tiles = (a.R + 127) / 128;
   const int per = (a.U + 7) / 8;
   const int64_t grid = (int64_t)8 * per * a.m_tiles;
   if (grid <= 0) return hipSuccess;
-  if (a.max_logits != nullptr)
-    hipLaunchKernelGGL((decode_spec128_kernel<DQK, true>), dim3((unsigned)grid), dim3(512), 0, s, a, per);
-  else
-    hipLaunchKernelGGL((decode_spec128_kernel<DQK, false>), dim3((unsigned)grid), dim3(512), 0, s, a, per);
-  return hipGetLastError();
+  return a.topk > 0 ? launch_tile128_t<DQK, true>(a, per, grid, s) : launch_tile128_t<DQK, false>(a, per, grid, s);
 }
 
 template <int DQK>
 hipError_t launch_dqk(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
-  if (sh.fmt == 0 && sh.R > 64) return launch_spec128<DQK>(a, s);  // bf16 rows, 65+ stacked rows
+  if (sh.fmt == 0 && sh.R > 64) return launch_tile128<DQK>(a, s);  // bf16 rows, 65+ stacked rows
   if (sh.fmt != 0) return launch_spec64<DQK, true>(a, s);  // fp8 rows: 64-row tiles for any R
   if (a.max_logits == nullptr) {  // the per-row maximum is produced by the 64-row kernel only
     if (sh.R <= 16) return launch_cfg<Cfg<16, 4, DQK>>(a, s);
