@@ -1398,6 +1398,7 @@ struct Tile128 {
   struct Soft {
     float m_ref[2], l_acc[2], m_top[2];  // per row tile: reference maximum, sum, true maximum
     float alpha[2], mu[2], lsum[2], mx[2], mnew[2], part[2];
+    float sink[2];  // sink logits of the split's rows (-inf: none)
     bool up[2];
     bf16x8 pf[2];  // P^T of the step
   };
@@ -1969,6 +1970,12 @@ struct Tile128 {
     int k = 0;
 #pragma unroll 1
     for (int ci = 0; ci < nc; ++ci) {
+      {
+        Lane Ls;
+        Ls.ln = lane_id();
+        Ls.v16 = 0;
+        load_sink(f.sink, desc(cq.ci, D_NSPLIT), Ls);
+      }
       if (ci > 0) {
         load_q(qr, cq.g);  // cq: the split's first step
 #pragma unroll
@@ -1999,7 +2006,7 @@ struct Tile128 {
       const float lt = rows_sum(f.l_acc[nt]);
       const int r = mt * 128 + 32 * wave + 16 * nt + nl;
       float lse_nat, scale;
-      row_norm(g, min(r, a.R - 1), f.m_ref[nt], lt, final_out, &lse_nat, &scale);
+      row_norm(f.sink[nt], f.m_ref[nt], lt, &lse_nat, &scale);
       if (gl == 0 && r < a.R) {
         st_global_b32(final_out ? a.lse + lse_index(g, r) : a.part_lse + (int64_t)split * a.R + r, lse_nat);
         if constexpr (MAXL) {  // natural-log units of the scaled scores
@@ -2034,16 +2041,13 @@ struct Tile128 {
     }
   }
 
-  // LSE (natural log) and output scale of a row; the sink is folded in for final outputs.
-  __device__ __forceinline__ void row_norm(int g, int r, float m2, float l, bool final_out,
-                                           float* lse_nat, float* scale) const {
+  // LSE (natural log) and output scale of a row; the sink logit sk (-inf: none) is folded in.
+  __device__ __forceinline__ void row_norm(float sk, float m2, float l, float* lse_nat, float* scale) const {
     const float kLn2 = 0.69314718055994530942f;
-    const float* sk_p = (final_out && a.sink != nullptr) ? a.sink + (sparse ? r : r % a.H) : nullptr;
     if (l > 0.f) {
       float lse = (m2 + __log2f(l)) * kLn2;
       float sc = 1.f / l;
-      if (sk_p != nullptr) {
-        const float sk = *sk_p;
+      if (sk != kNegInf) {
         const float mx = fmaxf(lse, sk);
         const float lse2 = mx + __logf(__expf(lse - mx) + __expf(sk - mx));
         sc *= __expf(lse - lse2);
@@ -2053,8 +2057,18 @@ struct Tile128 {
       *scale = sc;
     } else {
       *scale = 0.f;
-      *lse_nat = (sk_p != nullptr) ? *sk_p : kNegInf;
+      *lse_nat = sk;
     }
+  }
+  // Sink logits of the wave's two row tiles for a split's outputs (-inf: no sink, or partials that
+  // the combine finishes). Loaded between loops, where the pipeline waits for Q^T anyway.
+  __device__ __forceinline__ void load_sink(float (&sk)[2], int nsplit, const Lane& L) const {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = min(mt * 128 + 32 * wave + 16 * nt + (L.ln & 15), a.R - 1);
+      sk[nt] = (nsplit == 1 && a.sink != nullptr) ? a.sink[sparse ? r : r % a.H] : kNegInf;
+    }
+    asm volatile("" : "+v"(sk[0]), "+v"(sk[1]));  // the loads' wait here, not in the epilogue
   }
   __device__ __forceinline__ int64_t lse_index(int g, int r) const {
     int bb, t, h;
