@@ -723,9 +723,21 @@ __device__ __forceinline__ void mfma_o(f32x4& c, const bf16x8& a, const bf16x8& 
 __device__ __forceinline__ void mfma_o0(f32x4& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&a"(c) : "v"(a), "v"(b));
 }
-// 19 wait states: more than an XDL write -> VALU read of a 16x16x32 MFMA result needs.
-__device__ __forceinline__ void mfma_drain4(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& c3) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
+// The last k step of a 2 x 2 block of S^T tiles: its four MFMAs and the wait for their results
+// (19 wait states: more than an XDL write -> VALU read of a 16x16x32 result needs) in one statement. With the wait in a statement of its own, the compiler may place a copy of an
+// accumulator (a register move it inserts for the tied operands) between the MFMA and the wait,
+// where it would read the value before the MFMA has written it.
+__device__ __forceinline__ void mfma_s_last4(f32x4& c00, f32x4& c01, f32x4& c10, f32x4& c11,
+                                             const bf16x8& k0, const bf16x8& k1, const bf16x8& q0,
+                                             const bf16x8& q1) {
+  asm volatile(
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 2"
+      : "+v"(c00), "+v"(c01), "+v"(c10), "+v"(c11)
+      : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
 }
 // Score MFMAs with the Q^T operand held in accumulation registers.
 __device__ __forceinline__ void mfma_sq(f32x4& c, const bf16x8& a, const bf16x8& b) {
@@ -1789,7 +1801,7 @@ struct Tile128 {
         const int kt = m >> 1, nt = m & 1, sl = 4 * ks + m;
         if (ks + D - 1 < KS && nt == 0) ka[(ks + D - 1) % D][kt] = k_op(kt, ks + D - 1);
         if (ks == 0) mfma_s0(sacc[kt][nt], ka[ks % D][kt], qr[nt][ks]);
-        else mfma_s(sacc[kt][nt], ka[ks % D][kt], qr[nt][ks]);
+        else if (ks < KS - 1) mfma_s(sacc[kt][nt], ka[ks % D][kt], qr[nt][ks]);
         if constexpr (SOFT) {  // stages spread evenly over the 4 KS slots
 #pragma unroll
           for (int st = 0; st < kSoftStages; ++st)
@@ -1799,7 +1811,9 @@ struct Tile128 {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    mfma_drain4(sacc[0][0], sacc[0][1], sacc[1][0], sacc[1][1]);
+    constexpr int kl = (KS - 1) % D;
+    mfma_s_last4(sacc[0][0], sacc[0][1], sacc[1][0], sacc[1][1], ka[kl][0], ka[kl][1], qr[0][KS - 1],
+                 qr[1][KS - 1]);
   }
 
   // O^T (+)= V^T P^T of step x over all 512 output columns (FIRST: zero accumulator), with the rest
