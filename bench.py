@@ -10,7 +10,10 @@ option, --flush write). The step time (ms_per_step, value) brackets decode + com
 of events; a second loop with an event between the two kernels gives the per-kernel split
 (decode_ms, combine_ms) and the decode time the roofline uses — that middle event record delays the
 combine's dispatch, so the split sums to more than the step. Warm back-to-back figures are reported
-separately, eager and as a replayed HIP graph of the same steps. Prints one JSON line.
+separately, eager and as a replayed HIP graph of the same steps. The default run then times the
+other workloads (configs 3, 4, 5, s1, s4: median decode, combine and step µs, each against its own
+roofline) into a `per_config` object; their values are drawn on the GPU (workloads.make_on_device),
+since drawing s4's 1.3 GB cache on the host takes about a minute. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|1|3|4|5|s1|s4] [--no-cpu]
 """
@@ -55,6 +58,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the other workloads' decode timings (per_config)")
     ap.add_argument("--flush", choices=("read", "write"), default="read",
                     help="cache eviction before each timed step: read-only 1 GiB sweep (default) "
                          "or a 512 MB fill that leaves dirty lines in the Infinity Cache")
@@ -94,7 +99,7 @@ def algorithmic(wl):
     for b in range(B):
         Lb = int(L[b])
         if s.topk > 0:
-            idx = wl.indices[b].numpy()
+            idx = wl.indices[b].cpu().numpy()
             rows_b = set()
             for t in range(Sq):
                 ok = idx[t][(idx[t] >= 0) & (idx[t] < Lb)]
@@ -859,7 +864,107 @@ def main():
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if args.config is None and not args.no_per_config:
+        del q, cache, bt, runner, graph
+        torch.cuda.empty_cache()
+        res["per_config"] = per_config(args, evict)
     emit(res)
+
+
+PER_CONFIG = ("3", "4", "5", "s1", "s4")
+
+
+def per_config(args, evict):
+    """Decode and combine times of the other workloads (GPU only, values drawn on the device:
+    workloads.make_on_device), each against its own roofline."""
+    import torch
+    import mla_paged_latent_plan_amd as mla
+    from workloads import make_on_device
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out_all = {}
+    K = max(5, min(args.steps, 20))
+    for name in PER_CONFIG:
+        s = get_spec(name)
+        wl = make_on_device(s, dev)
+        p = mla.make_problem(s.batch, s.q_len, s.num_heads, s.d_qk,
+                             mla.MLA_KV_BF16 if s.kv_format == "bf16" else mla.MLA_KV_FP8,
+                             s.page_size, wl.page_stride, wl.num_pages, int(wl.block_table.shape[1]),
+                             s.topk, s.causal, s.window)
+        num_cus = s.plan_cus or mla.device_num_cus()
+        runner = mla.MLADecode(p, num_cus, device=dev)
+        seq = torch.from_numpy(wl.seqlens).to(dev)
+        out = torch.empty(s.batch, s.q_len, s.num_heads, s.d_v, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(s.batch, s.num_heads, s.q_len, dtype=torch.float32, device=dev)
+        mla.mla_decode_plan(p, num_cus, seq, None, runner.plan, stream)
+
+        def decode():
+            mla.mla_decode(p, num_cus, wl.q, wl.cache, wl.block_table, seq, s.sm_scale, wl.indices,
+                           wl.sink, runner.plan, runner.partials, out, lse, stream)
+
+        def combine():
+            mla.mla_combine(p, num_cus, runner.plan, runner.partials, wl.sink, out, lse, stream)
+
+        for _ in range(3):
+            decode()
+            combine()
+        torch.cuda.synchronize()
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        evs = [(ev(), ev(), ev()) for _ in range(K)]
+        for k in range(K):
+            if not args.no_flush:
+                evict(k)
+            a, m, e = evs[k]
+            a.record(stream)
+            decode()
+            m.record(stream)
+            combine()
+            e.record(stream)
+        torch.cuda.synchronize()
+        sevs = [(ev(), ev()) for _ in range(K)]
+        for k in range(K):
+            if not args.no_flush:
+                evict(k)
+            a, e = sevs[k]
+            a.record(stream)
+            decode()
+            combine()
+            e.record(stream)
+        torch.cuda.synchronize()
+        dec = np.array([a.elapsed_time(m) for a, m, _ in evs]) * 1e3
+        com = np.array([m.elapsed_time(e) for _, m, e in evs]) * 1e3
+        step = np.array([a.elapsed_time(e) for a, e in sevs]) * 1e3
+        alg = algorithmic(wl)
+        ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        bound = "hbm" if alg["flops"] / alg["bytes"] < ridge else "mfma"
+        dec_s = float(np.median(dec)) / 1e6
+        step_s = float(np.median(step)) / 1e6
+        if bound == "hbm":
+            frac = alg["bytes"] / dec_s / 1e9 / HBM_PEAK_GBS
+            sfrac = alg["bytes"] / step_s / 1e9 / HBM_PEAK_GBS
+        else:
+            frac = alg["flops"] / dec_s / 1e12 / MFMA_BF16_PEAK_TFS
+            sfrac = alg["flops"] / step_s / 1e12 / MFMA_BF16_PEAK_TFS
+        out_all[name] = {
+            "workload": s.name,
+            "decode_us_median": round(float(np.median(dec)), 2),
+            "combine_us_median": round(float(np.median(com)), 2),
+            "step_us_median": round(float(np.median(step)), 2),
+            "value": round(s.batch * s.q_len / step_s, 1),
+            "unit": "query tokens/s",
+            "bound": bound,
+            "frac": round(frac, 4),
+            "step_frac": round(sfrac, 4),
+            "hbm_tbs": round(alg["bytes"] / dec_s / 1e12, 3),
+            "mfma_tflops": round(alg["flops"] / dec_s / 1e12, 2),
+            "algorithmic_bytes": alg["bytes"],
+            "algorithmic_flops": alg["flops"],
+            "splits": int(runner.plan[:16].view(torch.int32)[3].item()),  # plan header word 3: the split count
+        }
+        del wl, runner, out, lse, seq
+        torch.cuda.empty_cache()
+    return out_all
 
 
 if __name__ == "__main__":

@@ -87,3 +87,24 @@ def test_configs_shapes():
     assert wl4.nope_codes.shape[1] == 448
     sc = wl4.scale_codes.numpy()
     assert sc[:, :7].min() >= 123 and sc[:, :7].max() <= 131 and np.all(sc[:, 7] == 0)
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+def test_device_draw_layout(spec):
+    """make_on_device (timing workloads) fills the same paged layout as make(): every logical row
+    written (no poison read back), fp8 exponents in range, every other byte 0xFF."""
+    from workloads import make_on_device
+    wl = make_on_device(spec, "cpu")
+    ref = make(spec)
+    assert np.array_equal(wl.seqlens, ref.seqlens)
+    assert wl.cache.shape == ref.cache.shape and wl.block_table.shape == ref.block_table.shape
+    bt = wl.block_table.numpy()
+    used = set()
+    for b in range(spec.batch):
+        L = int(wl.seqlens[b])
+        rows = paging.dense_rows(wl.cache.numpy(), bt, b, L, spec.kv_format, spec.d_qk,
+                                 spec.d_rope, spec.page_size)
+        assert rows.shape == (L, spec.d_qk) and np.all(np.isfinite(rows))
+        used.update(bt[b, :-(-L // spec.page_size)].tolist())
+    unused = [p for p in range(wl.num_pages) if p not in used]
+    assert len(unused) == spec.spare_pages and np.all(wl.cache.numpy()[unused] == 0xFF)

@@ -12,4 +12,5 @@ from .gen import (  # noqa: F401
     Workload,
     cache_layout,
     make,
+    make_on_device,
 )

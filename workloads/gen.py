@@ -180,7 +180,9 @@ def make(spec: Spec, seqlens: Optional[np.ndarray] = None,
         n = int(npages_req[b])
         block_table[b, :n] = perm[poff[b]:poff[b] + n]
 
-    cache = np.full((num_pages, stride), 0xFF if spec.poison else 0, dtype=np.uint8)
+    # torch's fill: numpy's takes seconds per hundred MB here
+    cache_t = torch.full((num_pages, stride), 0xFF if spec.poison else 0, dtype=torch.uint8)
+    cache = cache_t.numpy()
     if total > 0:
         req = np.repeat(np.arange(B), lens)
         pos = np.arange(total, dtype=np.int64) - off[req]
@@ -214,9 +216,87 @@ def make(spec: Spec, seqlens: Optional[np.ndarray] = None,
 
     return Workload(spec=spec, seqlens=seqlens, q=q, row_offsets=off, rows_bf16=rows_bf16,
                     nope_codes=nope, scale_codes=scales, rope_bf16=rope,
-                    cache=torch.from_numpy(cache), block_table=torch.from_numpy(block_table),
+                    cache=cache_t, block_table=torch.from_numpy(block_table),
                     page_stride=stride, indices=indices, topk_lens=tl, sink=sink)
 
+
+
+def make_on_device(spec: Spec, device) -> Workload:
+    """The workload of `spec` drawn on `device`, for timing only.
+
+    Same recipe as make(): the same request lengths, a random page permutation, values N(0, 1)
+    cast to the storage dtype, ue8m0 exponents uniform in the spec's range, top-k lists drawn
+    without replacement, 0xFF in every byte no row owns. The values come from the device's
+    generator, so they differ from make()'s (which the oracle reads); the logical row tensors are
+    not kept. Drawing a multi-GB cache this way takes milliseconds instead of a minute of host
+    time."""
+    g = torch.Generator().manual_seed(spec.seed)
+    seqlens = _draw_seqlens(spec, g)
+    gd = torch.Generator(device=device).manual_seed(spec.seed)
+    B, Sq, H, dqk, dr = spec.batch, spec.q_len, spec.num_heads, spec.d_qk, spec.d_rope
+    lay = cache_layout(spec.kv_format, dqk, dr, spec.page_size)
+    ps, row_bytes, stride = spec.page_size, lay["row_bytes"], lay["page_stride"]
+    q = torch.randn(B, Sq, H, dqk, generator=gd, device=device).to(torch.bfloat16)
+    lens = np.maximum(seqlens.astype(np.int64), 0)
+    off = np.zeros(B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lens)
+    total = int(off[-1])
+    npages_req = (lens + ps - 1) // ps
+    poff = np.zeros(B + 1, dtype=np.int64)
+    poff[1:] = np.cumsum(npages_req)
+    num_pages = int(poff[-1]) + spec.spare_pages
+    perm = torch.randperm(num_pages, generator=g).numpy().astype(np.int64)
+    max_pages = int(npages_req.max(initial=0)) + 1
+    spare_phys = perm[int(poff[-1])] if spec.spare_pages > 0 else perm[0]
+    block_table = np.full((B, max_pages), spare_phys, dtype=np.int32)
+    for b in range(B):
+        n = int(npages_req[b])
+        block_table[b, :n] = perm[poff[b]:poff[b] + n]
+    cache = torch.full((num_pages, stride), 0xFF if spec.poison else 0, dtype=torch.uint8, device=device)
+    if total > 0:
+        req = np.repeat(np.arange(B), lens)
+        pos = np.arange(total, dtype=np.int64) - off[req]
+        phys = torch.from_numpy(perm[poff[req] + pos // ps]).to(device)
+        slot = torch.from_numpy(pos % ps).to(device)
+        rview = cache.as_strided((num_pages, ps, row_bytes), (stride, row_bytes, 1))
+        chunk = 1 << 18  # rows per draw: bounds the fp32 temporaries
+        for a in range(0, total, chunk):
+            e = min(total, a + chunk)
+            ph, sl = phys[a:e], slot[a:e]
+            if spec.kv_format == "bf16":
+                rows = torch.randn(e - a, dqk, generator=gd, device=device).to(torch.bfloat16)
+                rview[ph, sl] = rows.view(torch.uint8).reshape(e - a, row_bytes)
+            else:
+                d_nope = lay["d_nope"]
+                ngrp = -(-d_nope // 64)
+                nope = torch.randn(e - a, d_nope, generator=gd, device=device).to(torch.float8_e4m3fn)
+                rope = torch.randn(e - a, dr, generator=gd, device=device).to(torch.bfloat16)
+                rv = rview[ph, sl]
+                rv[:, :d_nope] = nope.view(torch.uint8)
+                rv[:, d_nope:] = rope.view(torch.uint8).reshape(e - a, 2 * dr)
+                rview[ph, sl] = rv
+                lo, hi = spec.scale_exp_range
+                exps = torch.randint(lo, hi + 1, (e - a, ngrp), generator=gd, device=device)
+                sc = torch.zeros(e - a, SCALE_SLOT_BYTES, dtype=torch.uint8, device=device)
+                sc[:, :ngrp] = (127 + exps).to(torch.uint8)
+                sview = cache[:, lay["scale_offset"]:].as_strided(
+                    (num_pages, ps, SCALE_SLOT_BYTES), (stride, SCALE_SLOT_BYTES, 1))
+                sview[ph, sl] = sc
+    indices = None
+    if spec.topk > 0:
+        idx = torch.full((B, Sq, spec.topk), -1, dtype=torch.int32, device=device)
+        for b in range(B):
+            for t in range(Sq):
+                L = int(lens[b])
+                k = min(L, spec.topk)
+                if k > 0:
+                    idx[b, t, :k] = torch.randperm(L, generator=gd, device=device)[:k].to(torch.int32)
+        indices = idx
+    sink = torch.randn(H, generator=gd, device=device, dtype=torch.float32) if spec.sink else None
+    return Workload(spec=spec, seqlens=seqlens, q=q, row_offsets=off, rows_bf16=None,
+                    nope_codes=None, scale_codes=None, rope_bf16=None, cache=cache,
+                    block_table=torch.from_numpy(block_table).to(device), page_stride=stride,
+                    indices=indices, topk_lens=None, sink=sink)
 
 # ---- sparse prefill (FlashMLA wrapper, flash_mla_sparse_fwd) ----------------------------------
 
