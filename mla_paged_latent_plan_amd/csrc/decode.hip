@@ -47,9 +47,12 @@ constexpr int kStageA = kBlockRows * kRowStrideA;
 constexpr int kStageB = kBlockRows * 128;    // RoPE tails (64 bf16), XOR-swizzled
 constexpr float kNegInf = -__builtin_inff();
 // Lazy rescale threshold (log2 units): the reference maximum of a row moves, and O is rescaled, only
-// when the row maximum exceeds it by more than 2^16. Probabilities then stay below 2^16 (exact range
-// in bf16, relative rounding unchanged) and O below 2^16 x rows x max|V|, far inside fp32.
-constexpr float kTau = 16.0f;
+// when the row maximum exceeds it by more than 2^64. Probabilities then stay below 2^64 (bf16 keeps
+// its relative rounding at any magnitude) and O and l below 2^64 x rows x max|V|: inside fp32 for
+// max|V| up to 2^(64 - log2 rows) (2^47 at 128K rows). A smaller threshold rescales far more often
+// on fp8 rows with ue8m0 scales, whose scores spread over tens of log2 units (each rescale touches
+// all of a wave's O accumulators).
+constexpr float kTau = 64.0f;
 // The 16-row kernel reads each KV row once and takes it with the streaming (non-temporal) cache
 // policy (≈ 4 % faster at 16 heads). The 64-row kernel keeps the default policy: the second row
 // tile of a unit reads the same rows and finds them in L2 (the policy measured neutral there).
@@ -1361,16 +1364,31 @@ struct Spec64 {
 // validated when consumed. Bundles past the chunk's last step read the zero row, so every bundle
 // holds the same number of memory instructions and "bundle k has landed" is always the same
 // vmcnt (one later bundle in flight).
-template <int DQK, bool MAXL, bool SPARSE>
+//
+// fp8 rows (FP8, dense rows only): a bundle lands in a ring of three fp8 entries (e4m3 bytes, the
+// bf16 RoPE tail and the ue8m0 scale bytes of its 32 rows); at the start of its step the four waves
+// convert it once (each wave its own eight rows) into a bf16 slot of the layout above, after which
+// QK^T, softmax and PV run exactly as for bf16 rows. Two bf16 slots suffice (the step's QK^T and
+// the previous step's PV), which leaves room for the ring.
+template <int DQK, bool MAXL, bool SPARSE, bool FP8 = false>
 struct Tile128 {
+  static_assert(!FP8 || (!SPARSE && !MAXL), "fp8 rows: dense decode only");
   static constexpr bool HAS_B = DQK > 512;               // RoPE region present
   static constexpr int KS = DQK / 32;                    // 32-wide k steps of QK^T
   static constexpr int kRows = 32;                       // rows per slot / step
-  static constexpr int NS = 4;                           // slots
+  static constexpr int NS = FP8 ? 2 : 4;                 // bf16 slots
   static constexpr int kSlotA = kRows * kRowStrideA;
   static constexpr int kSlot = kSlotA + (HAS_B ? kRows * 128 : 0);
   static_assert(kSlot % 256 == 0, "slot bases keep the low byte of in-slot offsets");
-  static constexpr uint32_t kPgOff = NS * kSlot;         // block-table entries [4 waves][4 steps][8]
+  // fp8 ring entry: e4m3 bytes [32 rows][512] (kNope used), RoPE tails [32][128], scales [32][8]
+  static constexpr int kNope = DQK - 64;
+  static constexpr uint32_t kRingRope = kRows * 512;
+  static constexpr uint32_t kRingSc = kRingRope + kRows * 128;
+  static constexpr uint32_t kRingEntry = kRingSc + kRows * 8;
+  static_assert(kRingEntry % 256 == 0, "ring entries keep the low byte of in-entry offsets");
+  static constexpr int NR = 3;                           // fp8 ring entries
+  static constexpr uint32_t kRingOff = NS * kSlot;
+  static constexpr uint32_t kPgOff = kRingOff + (FP8 ? NR * kRingEntry : 0);  // block-table entries [4 waves][4 steps][8]
   static constexpr uint32_t kIxOff = kPgOff + 4 * 4 * 32;  // index entries [4 waves][8 steps][8]
   static constexpr uint32_t kMOff = kIxOff + 4 * 8 * 32;   // row-valid masks [8 steps][4 waves] bytes
   static constexpr uint32_t kDOff = kMOff + 32;           // split descriptors [kChunk][8 words]
@@ -1381,8 +1399,8 @@ struct Tile128 {
   static constexpr int kStageRow = HAS_B ? 544 : 528;     // epilogue staging: 256 columns + pad
   static_assert(4 * 16 * kStageRow <= kSlot, "epilogue staging fits in one slot");
   // memory instructions per bundle: 8 rows, the RoPE tails (+ with index lists the block-table and
-  // index dwords)
-  static constexpr int kNb = 8 + (HAS_B ? 1 : 0) + (SPARSE ? 2 : 0);
+  // index dwords); fp8 rows: 4 transfers of two rows' e4m3 bytes, the RoPE tails, the scale bytes
+  static constexpr int kNb = FP8 ? 6 : 8 + (HAS_B ? 1 : 0) + (SPARSE ? 2 : 0);
   static constexpr bool sparse = SPARSE;
   enum { D_G, D_B, D_J0, D_N, D_L, D_Q0, D_QEND, D_NSPLIT };
 
@@ -1405,6 +1423,7 @@ struct Tile128 {
   struct DAddr {
     uint64_t b0, b1;
     int isplit, nvalid;
+    uint64_t s0, s1;  // fp8 rows: the scale slots of row 0 on page e0 and of the first row on e1
   };
   // Softmax state of the split whose step is being finished, and the step's own values.
   struct Soft {
@@ -1550,15 +1569,34 @@ struct Tile128 {
                           (uint64_t)(slot * (uint32_t)a.row_bytes);
     return ok ? addr : (uint64_t)(uintptr_t)a.zero_row;
   }
+  __device__ __forceinline__ uint64_t scale_base(int e, uint32_t slot) const {
+    const bool ok = (e >= 0) & (e < num_pages32);
+    const uint64_t addr = (uint64_t)(uintptr_t)a.cache + (uint64_t)(uint32_t)e * (uint64_t)(uint32_t)a.page_stride +
+                          (uint64_t)a.scale_off + 8u * slot;
+    return ok ? addr : (uint64_t)(uintptr_t)a.zero_row;
+  }
   __device__ __forceinline__ DAddr dense_addr(const DRows& d) const {
     DAddr r;
     const int ps = 1 << a.ps_log2;
     const int in0 = d.j & (ps - 1);
     r.isplit = min(ps - in0, 8);
-    r.b0 = page_base((d.j >> a.ps_log2) < a.max_pages ? d.e0 : -1, (uint32_t)in0);
-    r.b1 = page_base(((d.j + 7) >> a.ps_log2) < a.max_pages ? d.e1 : -1, 0u);
+    const int e0 = (d.j >> a.ps_log2) < a.max_pages ? d.e0 : -1;
+    const int e1 = ((d.j + 7) >> a.ps_log2) < a.max_pages ? d.e1 : -1;
+    r.b0 = page_base(e0, (uint32_t)in0);
+    r.b1 = page_base(e1, 0u);
     r.nvalid = min(max(d.n - d.k, 0), 8);
+    if constexpr (FP8) {
+      r.s0 = scale_base(e0, (uint32_t)in0);
+      r.s1 = scale_base(e1, 0u);
+    }
     return r;
+  }
+  // Scale slot of dense fp8 row i, or the zero row.
+  __device__ __forceinline__ uint64_t drow_sc(const DAddr& r, int i) const {
+    const uint64_t on0 = r.s0 + (uint64_t)(uint32_t)(8 * i);
+    const uint64_t on1 = r.s1 + (uint64_t)(uint32_t)(8 * (i - r.isplit));
+    const uint64_t addr = (i < r.isplit) ? on0 : on1;
+    return (i < r.nvalid) ? addr : (uint64_t)(uintptr_t)a.zero_row;
   }
   // Address of dense row i (+ off), or of the zero row (+ off) when the row lies past the group's
   // rows or its page entry is out of range (then page_base gave the zero row).
@@ -1600,6 +1638,23 @@ struct Tile128 {
   // address read one transfer ahead into `next`), the RoPE tails, then the ring entries.
   __device__ __forceinline__ void send_part(int s, int y, Cur cp, Cur cx, uint64_t& next, const DAddr& d,
                                            const Lane& L) const {
+    if constexpr (FP8) {  // into ring entry y mod 3
+      const uint32_t re = kRingOff + (uint32_t)(y % NR) * kRingEntry;
+      const int ln = L.ln;
+      if (s < 4) {  // e4m3 bytes of rows 2s and 2s + 1: lanes 0-31 and 32-63, chunks swizzled
+        const uint64_t r0 = drow(d, 2 * s, 0), r1 = drow(d, 2 * s + 1, 0);
+        const int chunk = (ln & 31) ^ swz_ring(2 * s + (ln >> 5));
+        const uint64_t src = (ln < 32 ? r0 : r1) + (uint64_t)(16 * chunk);
+        dma_x4<kRowsNT>(reinterpret_cast<const void*>((uintptr_t)src), lds_addr(sm + re + (8 * wave + 2 * s) * 512));
+      } else if (s == 4) {  // RoPE tails: 16 bytes per lane, row ln >> 3
+        const uint64_t src = drow(d, ln >> 3, (uint32_t)kNope + 16u * (uint32_t)(ln & 7));
+        dma_x4<kRowsNT>(reinterpret_cast<const void*>((uintptr_t)src), lds_addr(sm + re + kRingRope + wave * 1024));
+      } else if (s == 5) {  // scale bytes: one dword per lane, lanes 0-15
+        const uint64_t src = drow_sc(d, (ln >> 1) & 7) + 4u * (uint32_t)(ln & 1);
+        if (ln < 16) dma_x1(reinterpret_cast<const int32_t*>((uintptr_t)src), lds_addr(sm + re + kRingSc + wave * 64));
+      }
+      return;
+    }
     const uint32_t sa = (uint32_t)(y & (NS - 1)) * kSlot;
     if constexpr (!SPARSE) {  // dense: addresses from the scalar block-table entries
       if (s < 8) {
@@ -1634,7 +1689,48 @@ struct Tile128 {
   __device__ __forceinline__ void send_all(int y, Cur cp, Cur cx, const DAddr& d, const Lane& L) const {
     uint64_t next = SPARSE ? rb_read(0) : 0;
 #pragma unroll
-    for (int s = 0; s < 11; ++s) send_part(s, y, cp, cx, next, d, L);
+    for (int s = 0; s < (FP8 ? kNb : 11); ++s) send_part(s, y, cp, cx, next, d, L);
+  }
+  // fp8 ring rows: 16-byte chunk c of row r sits at chunk c ^ swz_ring(r), so the conversion's
+  // reads (lane: row r, chunk 4 g + i) spread over all LDS banks.
+  __device__ __forceinline__ static int swz_ring(int r) { return r & 3; }
+  // fp8 rows: bundle x from its ring entry into bf16 slot x mod 2, each wave its eight rows. Lane
+  // (row 8w + (l >> 3), group l & 7) converts the group's 64 e4m3 values with its ue8m0 scale (for
+  // 512-wide rows group 7 is the RoPE tail, copied to latent columns 448-511), and copies one
+  // 16-byte chunk of the row's RoPE tail into the RoPE region when there is one. The 32 bf16 bytes
+  // of each source chunk are written as two 16-byte halves, the lanes of groups 2, 3, 6, 7 writing
+  // the upper half first: with the 1056-byte row stride that spreads each write over all banks.
+  __device__ __forceinline__ void convert(int x, const Lane& L) const {
+    const uint32_t re = kRingOff + (uint32_t)(x % NR) * kRingEntry;
+    const uint32_t dst = (uint32_t)(x & (NS - 1)) * kSlot;
+    const int ln = L.ln, r = 8 * wave + (ln >> 3), gi = ln & 7;
+    const uint32_t drow_off = dst + (uint32_t)r * kRowStrideA + 128u * (uint32_t)gi;
+    if (gi < kNope / 64) {
+      const uint32_t sw = *reinterpret_cast<const LDS_AS uint32_t*>(sm + re + kRingSc + 8 * r + (gi & 4));
+      const float sc = ue8m0_f32((sw >> (8 * (gi & 3))) & 0xFFu);
+      const uint32_t rrow = re + 512u * (uint32_t)r;
+      u32x4 w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = *reinterpret_cast<const LDS_AS u32x4*>(sm + rrow + 16 * ((4 * gi + i) ^ swz_ring(r)));
+      const bool up = (gi & 2) != 0;
+      const uint32_t h0 = up ? 16u : 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a0 = up ? w[i][2] : w[i][0], a1 = up ? w[i][3] : w[i][1];
+        const uint32_t b0 = up ? w[i][0] : w[i][2], b1 = up ? w[i][1] : w[i][3];
+        *reinterpret_cast<LDS_AS bf16x8*>(sm + drow_off + 32 * i + h0) = fp8x8_scaled(a0, a1, sc);
+        *reinterpret_cast<LDS_AS bf16x8*>(sm + drow_off + 32 * i + (16u - h0)) = fp8x8_scaled(b0, b1, sc);
+      }
+    } else {  // 512-wide rows: the RoPE tail is V's last 64 columns
+      const LDS_AS u32x4* src = reinterpret_cast<const LDS_AS u32x4*>(sm + re + kRingRope + 128 * r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<LDS_AS u32x4*>(sm + drow_off + 16 * i) = src[i];
+    }
+    if constexpr (HAS_B) {  // chunk gi of the tail at chunk gi ^ swz_b(r) of the RoPE region
+      const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(sm + re + kRingRope + 128 * r + 16 * gi);
+      *reinterpret_cast<LDS_AS u32x4*>(sm + dst + kSlotA + 128 * r + 16 * (gi ^ swz_b(r))) = v;
+    }
   }
   // bundle k landed, bundle k + 1 possibly still in flight
   __device__ __forceinline__ void wait_landed() const {
@@ -1872,11 +1968,15 @@ struct Tile128 {
                                             int cbase) {
     if constexpr (HAS_QK) wait_landed();
     lds_barrier();  // rows of step k visible; every wave is done with steps k - 2 (PV) and k - 1 (QK)
-    DAddr da;
-    if constexpr (HAS_QK && !SPARSE) da = dense_addr(dn);  // bundle k + 2 (entries loaded a step ago)
     Lane L;
     L.ln = lane_id();
     L.v16 = 16u * (uint32_t)L.ln;
+    if constexpr (FP8 && HAS_QK) {
+      convert(k, L);
+      lds_barrier();  // bf16 rows of step k complete
+    }
+    DAddr da;
+    if constexpr (HAS_QK && !SPARSE) da = dense_addr(dn);  // bundle k + 2 (entries loaded a step ago)
     if constexpr (HAS_PV) {
       if (cs.t == cs.q0) soft_reset(f);  // the softmax starts a new split
       apply_mask(sold, cs, k - 1, L);
@@ -2122,16 +2222,16 @@ __device__ __forceinline__ void unit_tile_blocked(int bid, int m_tiles, int per,
   *unit = x * per + q / m_tiles;
 }
 
-template <int DQK, bool MAXL, bool SPARSE>
+template <int DQK, bool MAXL, bool SPARSE, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_tile128_kernel(DecodeArgs a, int per) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[Tile128<DQK, MAXL, SPARSE>::LDS];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Tile128<DQK, MAXL, SPARSE, FP8>::LDS];
   int unit, mt;
   unit_tile_blocked(blockIdx.x, a.m_tiles, per, &unit, &mt);
   if (unit >= a.U || !plan_matches(a.plan, a.G, a.U, a.R)) return;
   const int s0 = a.plan[a.unit_ptr_off + unit];
   const int s1 = a.plan[a.unit_ptr_off + unit + 1];
-  Tile128<DQK, MAXL, SPARSE> d(a, (lds_ptr)lds, mt);
+  Tile128<DQK, MAXL, SPARSE, FP8> d(a, (lds_ptr)lds, mt);
   d.run_unit(s0, s1);
 }
 
@@ -2205,24 +2305,36 @@ hipError_t launch_spec64(DecodeArgs a, hipStream_t s) {
 template <int DQK, bool SPARSE>
 hipError_t launch_tile128_t(const DecodeArgs& a, int per, int64_t grid, hipStream_t s) {
   if (a.max_logits != nullptr)
-    hipLaunchKernelGGL((decode_tile128_kernel<DQK, true, SPARSE>), dim3((unsigned)grid), dim3(256), 0, s, a, per);
+    hipLaunchKernelGGL((decode_tile128_kernel<DQK, true, SPARSE, false>), dim3((unsigned)grid), dim3(256), 0, s, a, per);
   else
-    hipLaunchKernelGGL((decode_tile128_kernel<DQK, false, SPARSE>), dim3((unsigned)grid), dim3(256), 0, s, a, per);
+    hipLaunchKernelGGL((decode_tile128_kernel<DQK, false, SPARSE, false>), dim3((unsigned)grid), dim3(256), 0, s, a, per);
   return hipGetLastError();
 }
 template <int DQK>
-hipError_t launch_tile128(DecodeArgs a, hipStream_t s) {
+hipError_t launch_tile128(DecodeArgs a, hipStream_t s, bool fp8) {
   a.m_tiles = (a.R + 127) / 128;
   const int per = (a.U + 7) / 8;
   const int64_t grid = (int64_t)8 * per * a.m_tiles;
   if (grid <= 0) return hipSuccess;
+  if (fp8) {
+    hipLaunchKernelGGL((decode_tile128_kernel<DQK, false, false, true>), dim3((unsigned)grid), dim3(256), 0, s, a, per);
+    return hipGetLastError();
+  }
   return a.topk > 0 ? launch_tile128_t<DQK, true>(a, per, grid, s) : launch_tile128_t<DQK, false>(a, per, grid, s);
 }
 
 template <int DQK>
 hipError_t launch_dqk(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
-  if (sh.fmt == 0 && sh.R > 64) return launch_tile128<DQK>(a, s);  // bf16 rows, 65+ stacked rows
-  if (sh.fmt != 0) return launch_spec64<DQK, true>(a, s);  // fp8 rows: 64-row tiles for any R
+  if (sh.fmt == 0 && sh.R > 64) return launch_tile128<DQK>(a, s, false);  // bf16 rows, 65+ stacked rows
+  // fp8 rows, 65+ stacked rows, dense: converted once per step into bf16 slots; but windowed
+  // problems with under four blocks per unit (a few short splits per CU) run faster on 64-row
+  // tiles, whose per-split prologue and epilogue are half as long
+  if (sh.fmt != 0 && sh.R > 64 && a.topk == 0 && a.max_logits == nullptr) {
+    const int64_t win_blocks = (int64_t)(sh.window + sh.Sq - 1 + kBlockRows - 1) / kBlockRows + 1;
+    const bool tiny = sh.window > 0 && (int64_t)sh.G * win_blocks < 4 * (int64_t)sh.U;
+    if (!tiny) return launch_tile128<DQK>(a, s, true);
+  }
+  if (sh.fmt != 0) return launch_spec64<DQK, true>(a, s);  // other fp8 rows: 64-row tiles
   if (a.max_logits == nullptr) {  // the per-row maximum is produced by the 64-row kernel only
     if (sh.R <= 16) return launch_cfg<Cfg<16, 4, DQK>>(a, s);
     if (sh.R <= 32) return launch_cfg<Cfg<16, 2, DQK>>(a, s);
