@@ -2323,17 +2323,25 @@ hipError_t launch_tile128(DecodeArgs a, hipStream_t s, bool fp8) {
   return a.topk > 0 ? launch_tile128_t<DQK, true>(a, per, grid, s) : launch_tile128_t<DQK, false>(a, per, grid, s);
 }
 
+// 65+ stacked rows run on the 128-row tile unless the problem is known to give each unit under
+// four blocks (index lists of a few blocks, short windows, few groups): such short splits run
+// faster on 64-row tiles, whose per-split prologue (Q rows) and epilogue are half as long. Without
+// a window or index lists the row counts are only known on the device, and the 128-row tile is
+// taken.
+inline bool prefer_tile128(const Shape& sh) {
+  if (sh.R <= 64) return false;
+  int64_t blocks_per_group = -1;
+  if (sh.topk > 0) blocks_per_group = (sh.topk + kBlockRows - 1) / kBlockRows;
+  else if (sh.window > 0) blocks_per_group = (int64_t)(sh.window + sh.Sq - 1 + kBlockRows - 1) / kBlockRows + 1;
+  return blocks_per_group < 0 || (int64_t)sh.G * blocks_per_group >= 4 * (int64_t)sh.U;
+}
+
 template <int DQK>
 hipError_t launch_dqk(const DecodeArgs& a, const Shape& sh, hipStream_t s) {
-  if (sh.fmt == 0 && sh.R > 64) return launch_tile128<DQK>(a, s, false);  // bf16 rows, 65+ stacked rows
-  // fp8 rows, 65+ stacked rows, dense: converted once per step into bf16 slots; but windowed
-  // problems with under four blocks per unit (a few short splits per CU) run faster on 64-row
-  // tiles, whose per-split prologue and epilogue are half as long
-  if (sh.fmt != 0 && sh.R > 64 && a.topk == 0 && a.max_logits == nullptr) {
-    const int64_t win_blocks = (int64_t)(sh.window + sh.Sq - 1 + kBlockRows - 1) / kBlockRows + 1;
-    const bool tiny = sh.window > 0 && (int64_t)sh.G * win_blocks < 4 * (int64_t)sh.U;
-    if (!tiny) return launch_tile128<DQK>(a, s, true);
-  }
+  const bool t128 = prefer_tile128(sh);
+  if (sh.fmt == 0 && t128) return launch_tile128<DQK>(a, s, false);  // bf16 rows
+  // fp8 rows, dense: converted once per step into bf16 slots
+  if (sh.fmt != 0 && t128 && a.topk == 0 && a.max_logits == nullptr) return launch_tile128<DQK>(a, s, true);
   if (sh.fmt != 0) return launch_spec64<DQK, true>(a, s);  // other fp8 rows: 64-row tiles
   if (a.max_logits == nullptr) {  // the per-row maximum is produced by the 64-row kernel only
     if (sh.R <= 16) return launch_cfg<Cfg<16, 4, DQK>>(a, s);
