@@ -1691,19 +1691,21 @@ struct Tile128 {
 #pragma unroll
     for (int s = 0; s < (FP8 ? kNb : 11); ++s) send_part(s, y, cp, cx, next, d, L);
   }
-  // fp8 ring rows: 16-byte chunk c of row r sits at chunk c ^ swz_ring(r), so the conversion's
-  // reads (lane: row r, chunk 4 g + i) spread over all LDS banks.
-  __device__ __forceinline__ static int swz_ring(int r) { return r & 3; }
+  // fp8 ring rows: 16-byte chunk c of row r sits at chunk c ^ swz_ring(r), so each 16-lane quarter
+  // of the conversion's reads (lanes: rows r .. r + 7, chunk 4 g + i of two groups g) covers all
+  // LDS banks once.
+  __device__ __forceinline__ static int swz_ring(int r) { return ((r & 1) << 3) | ((r >> 1) & 3); }
   // fp8 rows: bundle x from its ring entry into bf16 slot x mod 2, each wave its eight rows. Lane
-  // (row 8w + (l >> 3), group l & 7) converts the group's 64 e4m3 values with its ue8m0 scale (for
+  // (row 8w + (l & 7), group l >> 3) converts the group's 64 e4m3 values with its ue8m0 scale (for
   // 512-wide rows group 7 is the RoPE tail, copied to latent columns 448-511), and copies one
   // 16-byte chunk of the row's RoPE tail into the RoPE region when there is one. The 32 bf16 bytes
-  // of each source chunk are written as two 16-byte halves, the lanes of groups 2, 3, 6, 7 writing
-  // the upper half first: with the 1056-byte row stride that spreads each write over all banks.
+  // of each source chunk are written as two 16-byte halves, the lanes of odd groups writing the
+  // upper half first: with the 1056-byte row stride each 16-lane quarter of a write then covers
+  // all banks once.
   __device__ __forceinline__ void convert(int x, const Lane& L) const {
     const uint32_t re = kRingOff + (uint32_t)(x % NR) * kRingEntry;
     const uint32_t dst = (uint32_t)(x & (NS - 1)) * kSlot;
-    const int ln = L.ln, r = 8 * wave + (ln >> 3), gi = ln & 7;
+    const int ln = L.ln, r = 8 * wave + (ln & 7), gi = ln >> 3;
     const uint32_t drow_off = dst + (uint32_t)r * kRowStrideA + 128u * (uint32_t)gi;
     if (gi < kNope / 64) {
       const uint32_t sw = *reinterpret_cast<const LDS_AS uint32_t*>(sm + re + kRingSc + 8 * r + (gi & 4));
@@ -1713,7 +1715,7 @@ struct Tile128 {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         w[i] = *reinterpret_cast<const LDS_AS u32x4*>(sm + rrow + 16 * ((4 * gi + i) ^ swz_ring(r)));
-      const bool up = (gi & 2) != 0;
+      const bool up = (gi & 1) != 0;
       const uint32_t h0 = up ? 16u : 0u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
