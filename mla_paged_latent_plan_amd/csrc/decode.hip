@@ -2084,16 +2084,15 @@ struct Tile128 {
     // whose wait the compiler would place among the MFMAs (such a wait would also hold for the row
     // transfers in flight).
     int k = 0;
+    {
+      Lane Ls;
+      Ls.ln = lane_id();
+      Ls.v16 = 0;
+      load_sink(f.sink, desc(cq.ci, D_NSPLIT), Ls);
+    }
 #pragma unroll 1
     for (int ci = 0; ci < nc; ++ci) {
-      {
-        Lane Ls;
-        Ls.ln = lane_id();
-        Ls.v16 = 0;
-        load_sink(f.sink, desc(cq.ci, D_NSPLIT), Ls);
-      }
       if (ci > 0) {
-        load_q(qr, cq.g);  // cq: the split's first step
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -2103,7 +2102,17 @@ struct Tile128 {
       iteration<true, false, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0);
 #pragma unroll 1
       for (++k; k < kend; ++k) iteration<true, true, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0);
+      // Q^T of the next split (cq: its first step) is requested before this split's last PV and
+      // epilogue, which no longer need the registers, so it lands while they run; its sink logits
+      // after the epilogue, which still reads this split's
+      if (ci + 1 < nc) load_q(qr, cq.g);
       iteration<false, true, true, false>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0);
+      if (ci + 1 < nc) {
+        Lane Ls;
+        Ls.ln = lane_id();
+        Ls.v16 = 0;
+        load_sink(f.sink, desc(cq.ci, D_NSPLIT), Ls);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the zero-row bundles past the end
   }
