@@ -9,10 +9,12 @@
 // mla_decode and are skipped. On request the row's largest scaled score is the largest of its
 // splits' (-inf without splits).
 //
-// Launch: one workgroup of 256 threads per (group, 4 query rows); 64 threads per row, each
-// owning 8 consecutive columns, so bf16 partial rows are read as contiguous 1 KB lines. Lane i reads
-// the LSE of split i (per chunk of 64 splits); eight splits' rows are loaded before they are
-// accumulated.
+// Launch: workgroups of 256 threads over (4 query rows, group); 64 threads per row, each owning 8
+// consecutive columns, so bf16 partial rows are read as contiguous 1 KB lines. Lane i reads the LSE
+// of split i (per chunk of 64 splits); eight splits' rows are loaded before they are accumulated.
+// Groups with more than one split number at most U - 1 (each straddles a unit boundary), so the
+// grid's group dimension is capped at U and a workgroup strides over groups; those with one split
+// (already final) cost it only their two split pointers.
 #include "mla_internal.h"
 
 namespace mla {
@@ -39,26 +41,54 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ void combine_group(const CombineArgs& a, int g, int s0, int s1);
+
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  const int g = blockIdx.y;
   if (!plan_matches(a.plan, a.G, a.U, a.R)) {
+#pragma unroll 1
     // a plan of another problem: the decode skipped its work, and every output row is NaN
-    const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (r >= a.R) return;
-    const int lane = threadIdx.x & 63;
-    const uint4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-    *reinterpret_cast<uint4*>(a.out + ((int64_t)g * a.R + r) * kDv + 8 * lane) = nan4;
-    if (lane == 0) {
-      const int b = a.sparse ? g / a.Sq : g, t = a.sparse ? g % a.Sq : r / a.H, h = a.sparse ? r : r % a.H;
-      a.lse[((int64_t)b * a.H + h) * a.Sq + t] = __builtin_nanf("");
-      if (a.max_logits != nullptr) a.max_logits[((int64_t)b * a.H + h) * a.Sq + t] = __builtin_nanf("");
+    for (int g = blockIdx.y; g < a.G; g += gridDim.y) {
+      const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+      if (r >= a.R) continue;
+      const int lane = threadIdx.x & 63;
+      const uint4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+      *reinterpret_cast<uint4*>(a.out + ((int64_t)g * a.R + r) * kDv + 8 * lane) = nan4;
+      if (lane == 0) {
+        const int b = a.sparse ? g / a.Sq : g, t = a.sparse ? g % a.Sq : r / a.H, h = a.sparse ? r : r % a.H;
+        a.lse[((int64_t)b * a.H + h) * a.Sq + t] = __builtin_nanf("");
+        if (a.max_logits != nullptr) a.max_logits[((int64_t)b * a.H + h) * a.Sq + t] = __builtin_nanf("");
+      }
     }
     return;
   }
-  const int s0 = __builtin_amdgcn_readfirstlane(a.plan[a.grp_ptr_off + g]);
-  const int s1 = __builtin_amdgcn_readfirstlane(a.plan[a.grp_ptr_off + g + 1]);
+  // the split pointers of the workgroup's first four groups are requested together
+  const int gstep = gridDim.y;
+  int p0[4], p1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = min((int)blockIdx.y + i * gstep, a.G - 1);
+    p0[i] = a.plan[a.grp_ptr_off + g];
+    p1[i] = a.plan[a.grp_ptr_off + g + 1];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = (int)blockIdx.y + i * gstep;
+    if (g < a.G) {
+      const int s0 = __builtin_amdgcn_readfirstlane(p0[i]), s1 = __builtin_amdgcn_readfirstlane(p1[i]);
+      if (s1 - s0 != 1) combine_group(a, g, s0, s1);
+    }
+  }
+#pragma unroll 1
+  for (int g = (int)blockIdx.y + 4 * gstep; g < a.G; g += gstep) {
+    const int s0 = __builtin_amdgcn_readfirstlane(a.plan[a.grp_ptr_off + g]);
+    const int s1 = __builtin_amdgcn_readfirstlane(a.plan[a.grp_ptr_off + g + 1]);
+    if (s1 - s0 != 1) combine_group(a, g, s0, s1);
+  }
+}
+
+// The merge of group g's splits [s0, s1) for the workgroup's four rows.
+__device__ __forceinline__ void combine_group(const CombineArgs& a, int g, int s0, int s1) {
   const int ns = s1 - s0;
-  if (ns == 1) return;
   const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (r >= a.R) return;
   const int lane = threadIdx.x & 63;
@@ -167,7 +197,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.G <= 0) return hipSuccess;
-  dim3 grid((a.R + kRowsPerBlock - 1) / kRowsPerBlock, a.G);
+  dim3 grid((a.R + kRowsPerBlock - 1) / kRowsPerBlock, (unsigned)min(a.G, max(a.U, 1)));
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
