@@ -62,6 +62,14 @@ CASES = {
     "fp8_sparse_h128": (Spec("fp8_sparse_h128", batch=2, q_len=1, num_heads=128, page_size=64,
                              kv_format="fp8", seqlens=(5000, 3), topk=300, sm_scale=S, seed=35),
                         None),
+    # 128 stacked rows with a causal window and a sink: the 128-row tile (fp8 ring conversion /
+    # bf16 slots) when planned on one CU, 64-row tiles when planned on the device (short windows)
+    "fp8_d512_h64_win_sink": (Spec("fp8_d512_h64_win_sink", batch=3, q_len=2, num_heads=64, d_qk=512,
+                                   kv_format="fp8", page_size=64, seqlens=(77, 700, 129), causal=True,
+                                   window=128, sink=True, sm_scale=1 / math.sqrt(512), seed=38), None),
+    "h64_sq2_win_sink": (Spec("h64_sq2_win_sink", batch=3, q_len=2, num_heads=64, page_size=64,
+                              seqlens=(5, 900, 200), causal=True, window=160, sink=True, sm_scale=S,
+                              seed=39), None),
     # a sink with empty contexts: O = 0 and LSE = the sink logit for those requests
     "sink_empty": (Spec("sink_empty", batch=4, q_len=1, num_heads=16, page_size=16,
                         seqlens=(0, 5, 0, 300), sink=True, sm_scale=S, seed=36), None),
