@@ -2032,9 +2032,19 @@ struct Tile128 {
   __device__ void run_chunk(int cb0) {
     const Cur c0 = cur_begin();
     Cur cb = c0, cp = c0, cx = c0;  // next bundle, block-table and index steps
-    // ---- prologue: Q^T of the first split, index and block-table entries, bundles 0-1 --------
+    // ---- prologue: Q^T and sink logits of the first split, index and block-table entries,
+    // bundles 0-1. Dense rows: Q^T, the sink logits and the bundles' rows are all in flight at
+    // once (their one wait follows the transfers). -----------------------------------------------
     bf16x8 qr[2][KS];
     load_q(qr, c0.g);
+    Soft f;
+    soft_reset(f);
+    {
+      Lane Ls;
+      Ls.ln = lane_id();
+      Ls.v16 = 0;
+      load_sink<false>(f.sink, desc(c0.ci, D_NSPLIT), Ls);
+    }
     if (sparse) {
 #pragma unroll 1
       for (int i = 0; i < 6; ++i) {
@@ -2042,19 +2052,13 @@ struct Tile128 {
         cx = cur_next(cx);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    if (sparse) {
 #pragma unroll 1
       for (int i = 0; i < 3; ++i) {
         dma_dword(page_src(cp), pg_slot(cp.y));
         cp = cur_next(cp);
       }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // entries in LDS before prepare reads them
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qr[nt][ks]));  // Q^T has landed
     DRows dn;
     Lane L0;
     L0.ln = lane_id();
@@ -2074,22 +2078,20 @@ struct Tile128 {
     if constexpr (SPARSE) prepare(cb, L0);  // bundle 2
     else dn = dense_rows(cb);
     cb = cur_next(cb);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qr[nt][ks]));  // Q^T has landed
+    asm volatile("" : "+v"(f.sink[0]), "+v"(f.sink[1]));
 
     f32x4 o[32][2];  // O^T: [output column tile][row tile], in accumulation registers
     f32x4 sold[2][2];
-    Soft f;
-    soft_reset(f);
     Cur cq = c0, cs = c0;
     // One pipelined loop per split. A split's Q^T is loaded between loops, so no loop holds a load
     // whose wait the compiler would place among the MFMAs (such a wait would also hold for the row
     // transfers in flight).
     int k = 0;
-    {
-      Lane Ls;
-      Ls.ln = lane_id();
-      Ls.v16 = 0;
-      load_sink(f.sink, desc(cq.ci, D_NSPLIT), Ls);
-    }
 #pragma unroll 1
     for (int ci = 0; ci < nc; ++ci) {
       if (ci > 0) {
@@ -2186,14 +2188,16 @@ struct Tile128 {
     }
   }
   // Sink logits of the wave's two row tiles for a split's outputs (-inf: no sink, or partials that
-  // the combine finishes). Loaded between loops, where the pipeline waits for Q^T anyway.
+  // the combine finishes). Loaded between loops, where the pipeline waits for Q^T anyway; PIN:
+  // the loads' wait right here (otherwise the caller's), not in the epilogue.
+  template <bool PIN = true>
   __device__ __forceinline__ void load_sink(float (&sk)[2], int nsplit, const Lane& L) const {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int r = min(mt * 128 + 32 * wave + 16 * nt + (L.ln & 15), a.R - 1);
       sk[nt] = (nsplit == 1 && a.sink != nullptr) ? a.sink[sparse ? r : r % a.H] : kNegInf;
     }
-    asm volatile("" : "+v"(sk[0]), "+v"(sk[1]));  // the loads' wait here, not in the epilogue
+    if constexpr (PIN) asm volatile("" : "+v"(sk[0]), "+v"(sk[1]));
   }
   __device__ __forceinline__ int64_t lse_index(int g, int r) const {
     int bb, t, h;
