@@ -1780,8 +1780,9 @@ struct Tile128 {
       int hi[2], lo[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        // the query's position pos = L - Sq + token (token = row / H), relative to the step offset
-        const int rel = c.L - a.Sq + (mt * 128 + 32 * wave + 16 * nt + nl) / a.H - c.j0 - kbase;
+        // the query's position pos = L - Sq + token (token = row / H), relative to the step offset;
+        // rows past R take row R - 1's (their Q^T is row R - 1's too)
+        const int rel = c.L - a.Sq + min(mt * 128 + 32 * wave + 16 * nt + nl, a.R - 1) / a.H - c.j0 - kbase;
         hi[nt] = a.causal ? rel : (1 << 30);
         lo[nt] = a.window > 0 ? rel - a.window + 1 : -(1 << 30);
       }
@@ -1961,14 +1962,21 @@ struct Tile128 {
 
   // One pipeline iteration k: QK^T of step k (cursor cq), softmax and PV of step k - 1 (cursor cs),
   // bundle k + 2 sent (its page and index steps: cp, cx), bundle k + 3 prepared (cursor cb; PREP);
-  // EPI: step k - 1 ends its split, whose rows are then normalised and stored. A split boundary
-  // splits iteration k in two: its PV part (EPI, no PREP) ends the old split, its QK part (no PV)
-  // starts the new one once that split's Q^T is loaded.
-  template <bool HAS_QK, bool HAS_PV, bool EPI, bool PREP>
+  // EPI: step k - 1 ends its split, whose rows are then normalised and stored (`pin` runs before
+  // the stores). A split boundary splits iteration k in two: its PV part (EPI, no PREP) ends the old
+  // split, its QK part (no PV) starts the new one once that split's Q^T is loaded. WAIT: bundle k
+  // may still be in flight (the first two steps of a split find their bundles landed: the
+  // prologue, or the pin of the previous split's epilogue, waited for every load so far).
+  struct NoPin {
+    __device__ __forceinline__ void operator()() const {}
+  };
+  template <bool HAS_QK, bool HAS_PV, bool EPI, bool PREP, class Pin = NoPin>
   __device__ __forceinline__ void iteration(int k, bf16x8 (&qr)[2][KS], f32x4 (&o)[32][2], f32x4 (&sold)[2][2],
                                             Soft& f, Cur& cq, Cur& cs, Cur& cb, Cur& cp, Cur& cx, DRows& dn,
-                                            int cbase) {
-    if constexpr (HAS_QK) wait_landed();
+                                            int cbase, bool wait, const Pin& pin = Pin()) {
+    if constexpr (HAS_QK) {
+      if (wait) wait_landed();
+    }
     lds_barrier();  // rows of step k visible; every wave is done with steps k - 2 (PV) and k - 1 (QK)
     Lane L;
     L.ln = lane_id();
@@ -2003,7 +2011,7 @@ struct Tile128 {
       if constexpr (PREP && SPARSE) prepare(cb, L);
       if constexpr (EPI) {  // the split's last step: normalise and store its rows
         lds_barrier();  // every wave is done reading slot k - 1: it stages the epilogue
-        epilogue(cbase + cs.ci, cs.g, desc(cs.ci, D_NSPLIT), (uint32_t)((k - 1) & (NS - 1)) * kSlot, o, f, L);
+        epilogue(cbase + cs.ci, cs.g, desc(cs.ci, D_NSPLIT), (uint32_t)((k - 1) & (NS - 1)) * kSlot, o, f, L, pin);
       }
     } else {
       // no PV: the transfers placed among the PV MFMAs go out here
@@ -2043,7 +2051,7 @@ struct Tile128 {
       Lane Ls;
       Ls.ln = lane_id();
       Ls.v16 = 0;
-      load_sink<false>(f.sink, desc(c0.ci, D_NSPLIT), Ls);
+      load_sink(f.sink, desc(c0.ci, D_NSPLIT), Ls);
     }
     if (sparse) {
 #pragma unroll 1
@@ -2094,21 +2102,24 @@ struct Tile128 {
     int k = 0;
 #pragma unroll 1
     for (int ci = 0; ci < nc; ++ci) {
-      if (ci > 0) {
+      const int k0 = k, kend = k + (cq.qend - cq.q0);
+      iteration<true, false, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, false);
+#pragma unroll 1
+      for (++k; k < kend; ++k) iteration<true, true, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, k > k0 + 1);
+      // Q^T of the next split (cq: its first step) is requested before this split's last PV and
+      // epilogue, which no longer need the registers, so it lands while they run. The epilogue waits
+      // for it (and so for every load issued so far) before its stores, and the next split's sink
+      // logits are requested after them, waited for only in its own epilogue: the stores drain
+      // while the next split's first two steps run, which wait for no load. (After a chunk's last
+      // split the epilogue's wait finds only zero-row bundles in flight.)
+      if (ci + 1 < nc) load_q(qr, cq.g);
+      auto pin = [&]() {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qr[nt][ks]));  // Q^T has landed
-      }
-      const int kend = k + (cq.qend - cq.q0);
-      iteration<true, false, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0);
-#pragma unroll 1
-      for (++k; k < kend; ++k) iteration<true, true, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0);
-      // Q^T of the next split (cq: its first step) is requested before this split's last PV and
-      // epilogue, which no longer need the registers, so it lands while they run; its sink logits
-      // after the epilogue, which still reads this split's
-      if (ci + 1 < nc) load_q(qr, cq.g);
-      iteration<false, true, true, false>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0);
+          for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qr[nt][ks]));
+      };
+      iteration<false, true, true, false>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, false, pin);
       if (ci + 1 < nc) {
         Lane Ls;
         Ls.ln = lane_id();
@@ -2116,37 +2127,43 @@ struct Tile128 {
         load_sink(f.sink, desc(cq.ci, D_NSPLIT), Ls);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the zero-row bundles past the end
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the epilogue's stores, zero-row bundles past the end
   }
 
   // Normalise the wave's 32 rows, stage them through slot LDS `stage` (16 rows x 256 columns at a
   // time) and store them as whole 128-byte lines, with their LSE; a group of one split gets its
-  // final outputs (sink folded in), others partials.
+  // final outputs (sink folded in), others partials. `pin` runs before the first store: it waits
+  // for the loads the next split needs, so that no later wait has to cover the stores.
+  //
+  // Every lane stores, whatever R: a row past R holds the same values as row R - 1 (same Q row,
+  // masks and sink; see load_q and apply_mask) and is stored there again, and the four lanes of a
+  // row store its LSE alike. Each epilogue thus issues the same stores, none of them behind a
+  // branch.
+  template <class Pin>
   __device__ __forceinline__ void epilogue(int split, int g, int nsplit, uint32_t stage, f32x4 (&o)[32][2],
-                                           const Soft& f, const Lane& L) const {
+                                           const Soft& f, const Lane& L, const Pin& pin) const {
     mfma_drain_acc(o);
     const bool final_out = (nsplit == 1);
     const uint32_t wst = stage + wave * 16 * kStageRow;
+    const int nl = L.ln & 15, gl = L.ln >> 4;
+    float lse_nat[2], scale[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) row_norm(f.sink[nt], f.m_ref[nt], rows_sum(f.l_acc[nt]), &lse_nat[nt], &scale[nt]);
+    pin();
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int nl = L.ln & 15, gl = L.ln >> 4;
-      const float lt = rows_sum(f.l_acc[nt]);
-      const int r = mt * 128 + 32 * wave + 16 * nt + nl;
-      float lse_nat, scale;
-      row_norm(f.sink[nt], f.m_ref[nt], lt, &lse_nat, &scale);
-      if (gl == 0 && r < a.R) {
-        st_global_b32(final_out ? a.lse + lse_index(g, r) : a.part_lse + (int64_t)split * a.R + r, lse_nat);
-        if constexpr (MAXL) {  // natural-log units of the scaled scores
-          const float ml = f.m_top[nt] * 0.69314718055994530942f;
-          st_global_b32(final_out ? a.max_logits + lse_index(g, r) : a.part_max + (int64_t)split * a.R + r, ml);
-        }
+      const int r = min(mt * 128 + 32 * wave + 16 * nt + nl, a.R - 1);
+      st_global_b32(final_out ? a.lse + lse_index(g, r) : a.part_lse + (int64_t)split * a.R + r, lse_nat[nt]);
+      if constexpr (MAXL) {  // natural-log units of the scaled scores
+        const float ml = f.m_top[nt] * 0.69314718055994530942f;
+        st_global_b32(final_out ? a.max_logits + lse_index(g, r) : a.part_max + (int64_t)split * a.R + r, ml);
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // lane (nl, gl): columns 16 ct + 4 gl .. + 3 of row nl, ct in [16h, 16h + 16)
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-          const f32x4 v = acc_read(o[16 * h + c][nt]) * scale;
+          const f32x4 v = acc_read(o[16 * h + c][nt]) * scale[nt];
           const u32x2 w = {(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
                            (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
           *reinterpret_cast<LDS_AS u32x2*>(sm + wst + nl * kStageRow + 32 * c + 8 * gl) = w;
@@ -2158,11 +2175,9 @@ struct Tile128 {
         for (int i = 0; i < 8; ++i) {
           const int row = 2 * i + (ln >> 5);
           const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(sm + wst + row * kStageRow + 16 * (ln & 31));
-          const int rr = mt * 128 + 32 * wave + 16 * nt + row;
-          if (rr < a.R) {
-            uint16_t* dst = final_out ? a.out + ((int64_t)g * a.R + rr) * kDv : a.part_o + ((int64_t)split * a.R + rr) * kDv;
-            st_global_b128(dst + 256 * h + 8 * (ln & 31), v);
-          }
+          const int rr = min(mt * 128 + 32 * wave + 16 * nt + row, a.R - 1);
+          uint16_t* dst = final_out ? a.out + ((int64_t)g * a.R + rr) * kDv : a.part_o + ((int64_t)split * a.R + rr) * kDv;
+          st_global_b128(dst + 256 * h + 8 * (ln & 31), v);
         }
       }
     }
@@ -2188,16 +2203,14 @@ struct Tile128 {
     }
   }
   // Sink logits of the wave's two row tiles for a split's outputs (-inf: no sink, or partials that
-  // the combine finishes). Loaded between loops, where the pipeline waits for Q^T anyway; PIN:
-  // the loads' wait right here (otherwise the caller's), not in the epilogue.
-  template <bool PIN = true>
+  // the combine finishes). No wait here: the compiler waits for them where they are used (the
+  // prologue's wait, or the epilogue before its stores).
   __device__ __forceinline__ void load_sink(float (&sk)[2], int nsplit, const Lane& L) const {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int r = min(mt * 128 + 32 * wave + 16 * nt + (L.ln & 15), a.R - 1);
       sk[nt] = (nsplit == 1 && a.sink != nullptr) ? a.sink[sparse ? r : r % a.H] : kNegInf;
     }
-    if constexpr (PIN) asm volatile("" : "+v"(sk[0]), "+v"(sk[1]));
   }
   __device__ __forceinline__ int64_t lse_index(int g, int r) const {
     int bb, t, h;
