@@ -1366,19 +1366,22 @@ struct Spec64 {
 // vmcnt (one later bundle in flight).
 //
 // fp8 rows (FP8, dense rows only): a bundle lands in a ring of three fp8 entries (e4m3 bytes, the
-// bf16 RoPE tail and the ue8m0 scale bytes of its 32 rows); at the start of its step the four waves
-// convert it once (each wave its own eight rows) into a bf16 slot of the layout above, after which
-// QK^T, softmax and PV run exactly as for bf16 rows. Two bf16 slots suffice (the step's QK^T and
-// the previous step's PV), which leaves room for the ring.
+// bf16 RoPE tail and the ue8m0 scale bytes of its 32 rows) and is converted once into a bf16 slot
+// of the layout above (latent values only; QK^T reads the RoPE tail from the ring entry, where its
+// 16-byte chunks land swizzled as in a RoPE region). Each wave converts its own eight rows of step
+// k + 1 between the PV MFMAs of iteration k, after waiting for its own transfers of that bundle, so
+// the conversion runs in the MFMA pipe's shadow and the step keeps its one barrier. Three bf16
+// slots (QK^T of step k, PV of step k - 1, conversion of step k + 1) and the ring fill the LDS; the
+// block-table and index tables, which only index lists need, are left out.
 template <int DQK, bool MAXL, bool SPARSE, bool FP8 = false>
 struct Tile128 {
   static_assert(!FP8 || (!SPARSE && !MAXL), "fp8 rows: dense decode only");
   static constexpr bool HAS_B = DQK > 512;               // RoPE region present
   static constexpr int KS = DQK / 32;                    // 32-wide k steps of QK^T
   static constexpr int kRows = 32;                       // rows per slot / step
-  static constexpr int NS = FP8 ? 2 : 4;                 // bf16 slots
+  static constexpr int NS = FP8 ? 3 : 4;                 // bf16 slots
   static constexpr int kSlotA = kRows * kRowStrideA;
-  static constexpr int kSlot = kSlotA + (HAS_B ? kRows * 128 : 0);
+  static constexpr int kSlot = kSlotA + ((HAS_B && !FP8) ? kRows * 128 : 0);
   static_assert(kSlot % 256 == 0, "slot bases keep the low byte of in-slot offsets");
   // fp8 ring entry: e4m3 bytes [32 rows][512] (kNope used), RoPE tails [32][128], scales [32][8]
   static constexpr int kNope = DQK - 64;
@@ -1388,19 +1391,26 @@ struct Tile128 {
   static_assert(kRingEntry % 256 == 0, "ring entries keep the low byte of in-entry offsets");
   static constexpr int NR = 3;                           // fp8 ring entries
   static constexpr uint32_t kRingOff = NS * kSlot;
-  static constexpr uint32_t kPgOff = kRingOff + (FP8 ? NR * kRingEntry : 0);  // block-table entries [4 waves][4 steps][8]
-  static constexpr uint32_t kIxOff = kPgOff + 4 * 4 * 32;  // index entries [4 waves][8 steps][8]
-  static constexpr uint32_t kMOff = kIxOff + 4 * 8 * 32;   // row-valid masks [8 steps][4 waves] bytes
-  static constexpr uint32_t kDOff = kMOff + 32;           // split descriptors [kChunk][8 words]
-  static constexpr int kChunk = 16;
-  static constexpr uint32_t kRbOff = kDOff + kChunk * 32;  // next bundle's row addresses [4 waves][8]
-  static constexpr int LDS = kRbOff + 4 * 64;
+  // index lists only: block-table entries [4 waves][4 steps][8], index entries [4 waves][8 steps][8],
+  // row-valid masks [8 steps][4 waves] bytes, the next bundle's row addresses [4 waves][8]
+  static constexpr uint32_t kPgOff = kRingOff + (FP8 ? NR * kRingEntry : 0);
+  static constexpr uint32_t kIxOff = kPgOff + (SPARSE ? 4 * 4 * 32 : 0);
+  static constexpr uint32_t kMOff = kIxOff + (SPARSE ? 4 * 8 * 32 : 0);
+  static constexpr uint32_t kDOff = kMOff + (SPARSE ? 32 : 0);  // split descriptors [kChunk][8 words]
+  static constexpr int kChunk = FP8 ? 8 : 16;
+  static constexpr uint32_t kRbOff = kDOff + kChunk * 32;
+  static constexpr int LDS = kRbOff + (SPARSE ? 4 * 64 : 0);
   static_assert(LDS <= 160 * 1024, "LDS of one workgroup");
-  static constexpr int kStageRow = HAS_B ? 544 : 528;     // epilogue staging: 256 columns + pad
+  static constexpr int kStageRow = (HAS_B && !FP8) ? 544 : 528;  // epilogue staging: 256 columns + pad
   static_assert(4 * 16 * kStageRow <= kSlot, "epilogue staging fits in one slot");
   // memory instructions per bundle: 8 rows, the RoPE tails (+ with index lists the block-table and
   // index dwords); fp8 rows: 4 transfers of two rows' e4m3 bytes, the RoPE tails, the scale bytes
   static constexpr int kNb = FP8 ? 6 : 8 + (HAS_B ? 1 : 0) + (SPARSE ? 2 : 0);
+  // LDS offsets of bf16 slot x and fp8 ring entry x
+  __device__ __forceinline__ static uint32_t slot_off(int x) {
+    return (uint32_t)(NS == 4 ? (x & 3) : (x % NS)) * (uint32_t)kSlot;
+  }
+  __device__ __forceinline__ static uint32_t ring_off(int x) { return kRingOff + (uint32_t)(x % NR) * kRingEntry; }
   static constexpr bool sparse = SPARSE;
   enum { D_G, D_B, D_J0, D_N, D_L, D_Q0, D_QEND, D_NSPLIT };
 
@@ -1639,15 +1649,17 @@ struct Tile128 {
   __device__ __forceinline__ void send_part(int s, int y, Cur cp, Cur cx, uint64_t& next, const DAddr& d,
                                            const Lane& L) const {
     if constexpr (FP8) {  // into ring entry y mod 3
-      const uint32_t re = kRingOff + (uint32_t)(y % NR) * kRingEntry;
+      const uint32_t re = ring_off(y);
       const int ln = L.ln;
       if (s < 4) {  // e4m3 bytes of rows 2s and 2s + 1: lanes 0-31 and 32-63, chunks swizzled
         const uint64_t r0 = drow(d, 2 * s, 0), r1 = drow(d, 2 * s + 1, 0);
         const int chunk = (ln & 31) ^ swz_ring(2 * s + (ln >> 5));
         const uint64_t src = (ln < 32 ? r0 : r1) + (uint64_t)(16 * chunk);
         dma_x4<kRowsNT>(reinterpret_cast<const void*>((uintptr_t)src), lds_addr(sm + re + (8 * wave + 2 * s) * 512));
-      } else if (s == 4) {  // RoPE tails: 16 bytes per lane, row ln >> 3
-        const uint64_t src = drow(d, ln >> 3, (uint32_t)kNope + 16u * (uint32_t)(ln & 7));
+      } else if (s == 4) {  // RoPE tails: 16 bytes per lane, row ln >> 3 (chunks swizzled for QK^T)
+        const int i2 = ln >> 3;
+        const int ch = HAS_B ? ((ln & 7) ^ swz_b(8 * wave + i2)) : (ln & 7);
+        const uint64_t src = drow(d, i2, (uint32_t)kNope + 16u * (uint32_t)ch);
         dma_x4<kRowsNT>(reinterpret_cast<const void*>((uintptr_t)src), lds_addr(sm + re + kRingRope + wave * 1024));
       } else if (s == 5) {  // scale bytes: one dword per lane, lanes 0-15
         const uint64_t src = drow_sc(d, (ln >> 1) & 7) + 4u * (uint32_t)(ln & 1);
@@ -1655,7 +1667,7 @@ struct Tile128 {
       }
       return;
     }
-    const uint32_t sa = (uint32_t)(y & (NS - 1)) * kSlot;
+    const uint32_t sa = slot_off(y);
     if constexpr (!SPARSE) {  // dense: addresses from the scalar block-table entries
       if (s < 8) {
         dma_x4s<kRowsNT>(L.v16, drow(d, s, 0), lds_addr(sm + sa + (8 * wave + s) * kRowStrideA));
@@ -1695,46 +1707,75 @@ struct Tile128 {
   // of the conversion's reads (lanes: rows r .. r + 7, chunk 4 g + i of two groups g) covers all
   // LDS banks once.
   __device__ __forceinline__ static int swz_ring(int r) { return ((r & 1) << 3) | ((r >> 1) & 3); }
-  // fp8 rows: bundle x from its ring entry into bf16 slot x mod 2, each wave its eight rows. Lane
-  // (row 8w + (l & 7), group l >> 3) converts the group's 64 e4m3 values with its ue8m0 scale (for
-  // 512-wide rows group 7 is the RoPE tail, copied to latent columns 448-511), and copies one
-  // 16-byte chunk of the row's RoPE tail into the RoPE region when there is one. The 32 bf16 bytes
-  // of each source chunk are written as two 16-byte halves, the lanes of odd groups writing the
-  // upper half first: with the 1056-byte row stride each 16-lane quarter of a write then covers
-  // all banks once.
-  __device__ __forceinline__ void convert(int x, const Lane& L) const {
-    const uint32_t re = kRingOff + (uint32_t)(x % NR) * kRingEntry;
-    const uint32_t dst = (uint32_t)(x & (NS - 1)) * kSlot;
+  // fp8 rows: bundle x from its ring entry into bf16 slot x mod 3, each wave its eight rows, in
+  // kCvStages stages of at most one LDS access or a few VALU instructions, so they can sit between
+  // MFMAs. Lane (row r = 8w + (l & 7), group gi = l >> 3) converts the group's 64 e4m3 values with
+  // its ue8m0 scale: stage 0 reads the scale dword, 1-4 the four 16-byte source chunks, 5 forms the
+  // scale, then each of the eight 16-byte writes takes three stages (two conversions of four
+  // values, the write). For 512-wide rows group 7 is the RoPE tail, which those lanes copy to latent
+  // columns 448-511 (a chunk read in the write's first stage). Each 16-lane quarter of a write meets
+  // two-way bank conflicts (two groups 128 bytes apart); writing odd groups' upper halves first
+  // would avoid them but its lane-dependent selects cost more than the conflicts.
+  static constexpr int NG = kNope / 64;  // groups of e4m3 values per row
+  static constexpr int kCvStages = 6 + 3 * 8;
+  struct Cv {
+    uint32_t sw;  // the row's scale dword holding the group's byte
+    float sc;     // the group's scale
+    u32x4 w[4];   // the group's e4m3 bytes
+    bf16x8 x;     // the write in progress
+    u32x4 rp;     // 512-wide rows, group 7: the RoPE chunk of the write in progress
+  };
+  __device__ __forceinline__ void cv_stage(int st, Cv& c, int x, const Lane& L) const {
     const int ln = L.ln, r = 8 * wave + (ln & 7), gi = ln >> 3;
-    const uint32_t drow_off = dst + (uint32_t)r * kRowStrideA + 128u * (uint32_t)gi;
-    if (gi < kNope / 64) {
-      const uint32_t sw = *reinterpret_cast<const LDS_AS uint32_t*>(sm + re + kRingSc + 8 * r + (gi & 4));
-      const float sc = ue8m0_f32((sw >> (8 * (gi & 3))) & 0xFFu);
-      const uint32_t rrow = re + 512u * (uint32_t)r;
-      u32x4 w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = *reinterpret_cast<const LDS_AS u32x4*>(sm + rrow + 16 * ((4 * gi + i) ^ swz_ring(r)));
-      const bool up = (gi & 1) != 0;
-      const uint32_t h0 = up ? 16u : 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t a0 = up ? w[i][2] : w[i][0], a1 = up ? w[i][3] : w[i][1];
-        const uint32_t b0 = up ? w[i][0] : w[i][2], b1 = up ? w[i][1] : w[i][3];
-        *reinterpret_cast<LDS_AS bf16x8*>(sm + drow_off + 32 * i + h0) = fp8x8_scaled(a0, a1, sc);
-        *reinterpret_cast<LDS_AS bf16x8*>(sm + drow_off + 32 * i + (16u - h0)) = fp8x8_scaled(b0, b1, sc);
+    const uint32_t re = ring_off(x);
+    if (st == 0) {
+      c.sw = *reinterpret_cast<const LDS_AS uint32_t*>(sm + re + kRingSc + 8 * r + (gi & 4));
+    } else if (st <= 4) {
+      const int i = st - 1;
+      c.w[i] = *reinterpret_cast<const LDS_AS u32x4*>(sm + re + 512u * (uint32_t)r + 16 * ((4 * gi + i) ^ swz_ring(r)));
+    } else if (st == 5) {
+      c.sc = ue8m0_f32((c.sw >> (8 * (gi & 3))) & 0xFFu);
+    } else {
+      const int j = (st - 6) / 3, sub = (st - 6) % 3, i = j >> 1;
+      const bool hi = (j & 1) != 0;  // this write: the upper 16 bytes of pair i
+      if (sub == 0) {
+        if constexpr (!HAS_B) {
+          if (gi >= NG)
+            c.rp = *reinterpret_cast<const LDS_AS u32x4*>(sm + re + kRingRope + 128u * (uint32_t)r + 16 * (2 * i + (hi ? 1 : 0)));
+        }
+        const uint32_t w0 = hi ? c.w[i][2] : c.w[i][0];
+        const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, c.sc, false);
+        const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, c.sc, true);
+        c.x[0] = a0[0];
+        c.x[1] = a0[1];
+        c.x[2] = a1[0];
+        c.x[3] = a1[1];
+      } else if (sub == 1) {
+        const uint32_t w1 = hi ? c.w[i][3] : c.w[i][1];
+        const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, c.sc, false);
+        const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, c.sc, true);
+        c.x[4] = a2[0];
+        c.x[5] = a2[1];
+        c.x[6] = a3[0];
+        c.x[7] = a3[1];
+      } else {
+        u32x4 v = __builtin_bit_cast(u32x4, c.x);
+        if constexpr (!HAS_B) v = (gi < NG) ? v : c.rp;
+        const uint32_t dst = slot_off(x) + (uint32_t)r * kRowStrideA + 128u * (uint32_t)gi + 32u * (uint32_t)i + (hi ? 16u : 0u);
+        *reinterpret_cast<LDS_AS u32x4*>(sm + dst) = v;
       }
-    } else {  // 512-wide rows: the RoPE tail is V's last 64 columns
-      const LDS_AS u32x4* src = reinterpret_cast<const LDS_AS u32x4*>(sm + re + kRingRope + 128 * r);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<LDS_AS u32x4*>(sm + drow_off + 16 * i) = src[i];
-    }
-    if constexpr (HAS_B) {  // chunk gi of the tail at chunk gi ^ swz_b(r) of the RoPE region
-      const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(sm + re + kRingRope + 128 * r + 16 * gi);
-      *reinterpret_cast<LDS_AS u32x4*>(sm + dst + kSlotA + 128 * r + 16 * (gi ^ swz_b(r))) = v;
     }
   }
-  // bundle k landed, bundle k + 1 possibly still in flight
+  // PV slot (0-63) of conversion stage st
+  __device__ __forceinline__ static constexpr int cv_slot(int st) { return (st * 64) / kCvStages; }
+  __device__ __forceinline__ void convert_all(int x, const Lane& L) const {
+    Cv c;
+#pragma unroll
+    for (int st = 0; st < kCvStages; ++st) cv_stage(st, c, x, L);
+  }
+  // bundle k landed, bundle k + 1 possibly still in flight (fp8 rows: the wave's own transfers of
+  // bundle k + 1, the input of its conversion, landed; those of bundle k + 2, all issued among the
+  // QK^T MFMAs, possibly in flight)
   __device__ __forceinline__ void wait_landed() const {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kNb) : "memory");
   }
@@ -1760,7 +1801,7 @@ struct Tile128 {
   __device__ __forceinline__ void apply_mask(f32x4 (&s)[2][2], Cur c, int x, const Lane& L) const {
     const int ln = L.ln;
     const int nl = ln & 15, gl = ln >> 4;
-    const uint32_t vmask = *reinterpret_cast<const LDS_AS uint32_t*>(sm + kMOff + 4 * (x & 7));
+    const uint32_t vmask = sparse ? *reinterpret_cast<const LDS_AS uint32_t*>(sm + kMOff + 4 * (x & 7)) : ~0u;
     const bool dense_mask = !sparse && (a.causal || a.window > 0);
     const bool need = sparse ? (vmask != ~0u) : (kRows * (c.t + 1) > c.n || dense_mask);
     if (!need) return;
@@ -1859,9 +1900,10 @@ struct Tile128 {
 
   // Side work of MFMA slot sl of an iteration (0 .. 4 KS - 1: QK^T, then 64 PV slots): the
   // transfers of the bundle being sent, one every kDmaGap slots, so the CU's LDS-DMA unit (about one
-  // 1 KB transfer per 46 cycles) sees an even stream instead of bursts.
+  // 1 KB transfer per 46 cycles) sees an even stream instead of bursts. fp8 rows send all of a
+  // bundle among the QK^T MFMAs (the PV slots carry the conversion).
   static constexpr int kSlots = 4 * KS + 64;
-  static constexpr int kDmaGap = kSlots / kNb;
+  static constexpr int kDmaGap = (FP8 ? 4 * KS : kSlots) / kNb;  // fp8 rows: all among QK^T
   __device__ __forceinline__ int dma_part(int i) const { return (i < 8 || HAS_B) ? i : i + 1; }
   template <bool SEND>
   __device__ __forceinline__ void side_dma(int sl, int y, Cur cp, Cur cx, uint64_t& next, const DAddr& d,
@@ -1871,15 +1913,16 @@ struct Tile128 {
     }
   }
 
-  // S^T = K Q^T of step x (slot x % 4), with the softmax micro-stages of the previous step (SOFT)
-  // and the first transfers of bundle y (SEND) between the MFMAs.
+  // S^T = K Q^T of step x (slot x mod NS; fp8 rows: the RoPE part from ring entry x mod 3), with
+  // the softmax micro-stages of the previous step (SOFT) and the first transfers of bundle y (SEND)
+  // between the MFMAs.
   template <bool SOFT, bool SEND>
   __device__ __forceinline__ void qk(f32x4 (&sacc)[2][2], const bf16x8 (&qr)[2][KS], int x, Soft& f,
                                     const f32x4 (&sold)[2][2], int y, Cur cp, Cur cx, const DAddr& d,
                                     uint64_t& next, const Lane& L) const {
     const int nl = L.ln & 15, gl = L.ln >> 4;
-    const uint32_t sa = (uint32_t)(x & (NS - 1)) * kSlot;
-    const uint32_t sb = sa + kSlotA;
+    const uint32_t sa = slot_off(x);
+    const uint32_t sb = FP8 ? ring_off(x) + kRingRope : sa + kSlotA;
     const uint32_t kaddr = sa + nl * kRowStrideA + 16 * gl;
     auto k_op = [&](int kt, int ks) -> bf16x8 {
       if (ks < 16) return lds_read_b128(sm, kaddr + 16 * kt * kRowStrideA + 64 * ks);
@@ -1916,12 +1959,17 @@ struct Tile128 {
   }
 
   // O^T (+)= V^T P^T of step x over all 512 output columns (FIRST: zero accumulator), with the rest
-  // of bundle y's transfers between the MFMAs (SEND).
-  template <bool FIRST, bool PREP, bool SEND>
+  // of bundle y's transfers between the MFMAs (SEND), or with fp8 rows the conversion of bundle
+  // x + 2 (CV; WAIT: its transfers may still be in flight).
+  template <bool FIRST, bool PREP, bool SEND, bool CV>
   __device__ __forceinline__ void pv(f32x4 (&o)[32][2], const bf16x8 (&pf)[2], int x, Cur c, int y, Cur cp,
-                                    Cur cx, const DAddr& d, uint64_t& next, const Lane& L) const {
+                                    Cur cx, const DAddr& d, uint64_t& next, const Lane& L, bool wait) const {
     const int nl = L.ln & 15, gl = L.ln >> 4;
-    const uint32_t sa = (uint32_t)(x & (NS - 1)) * kSlot;
+    const uint32_t sa = slot_off(x);
+    Cv cv;
+    if constexpr (CV) {
+      if (wait) wait_landed();
+    }
     const uint32_t vbase = sa + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (nl & 3);
     auto v_op = [&](int ct) -> bf16x8 {
       const uint32_t ad = vbase + 32 * ct;
@@ -1942,6 +1990,11 @@ struct Tile128 {
         if (FIRST) mfma_o0(o[ct][nt], va[ct % VD], pf[nt]);
         else mfma_o(o[ct][nt], va[ct % VD], pf[nt]);
         side_dma<SEND>(sl, y, cp, cx, next, d, L);
+        if constexpr (CV) {
+#pragma unroll
+          for (int st = 0; st < kCvStages; ++st)
+            if (cv_slot(st) == 2 * ct + nt) cv_stage(st, cv, x + 2, L);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1974,17 +2027,15 @@ struct Tile128 {
   __device__ __forceinline__ void iteration(int k, bf16x8 (&qr)[2][KS], f32x4 (&o)[32][2], f32x4 (&sold)[2][2],
                                             Soft& f, Cur& cq, Cur& cs, Cur& cb, Cur& cp, Cur& cx, DRows& dn,
                                             int cbase, bool wait, const Pin& pin = Pin()) {
-    if constexpr (HAS_QK) {
+    if constexpr (HAS_QK && !FP8) {
       if (wait) wait_landed();
     }
-    lds_barrier();  // rows of step k visible; every wave is done with steps k - 2 (PV) and k - 1 (QK)
+    // rows of step k visible (fp8 rows: converted in the previous iteration); every wave is done with
+    // steps k - 2 (PV) and k - 1 (QK)
+    lds_barrier();
     Lane L;
     L.ln = lane_id();
     L.v16 = 16u * (uint32_t)L.ln;
-    if constexpr (FP8 && HAS_QK) {
-      convert(k, L);
-      lds_barrier();  // bf16 rows of step k complete
-    }
     DAddr da;
     if constexpr (HAS_QK && !SPARSE) da = dense_addr(dn);  // bundle k + 2 (entries loaded a step ago)
     if constexpr (HAS_PV) {
@@ -2005,19 +2056,24 @@ struct Tile128 {
       const bool first = cs.t == cs.q0;
       if (!first) rescale(o, f);
       asm volatile("s_nop 4" ::: "memory");  // P^T written by VALU, O^T rescaled: wait states
-      if (first) pv<true, PREP, HAS_QK>(o, f.pf, k - 1, cb, ysend, cp, cx, da, next, L);
-      else pv<false, PREP, HAS_QK>(o, f.pf, k - 1, cb, ysend, cp, cx, da, next, L);
+      // fp8 rows: bundle k + 1 converted among the MFMAs (its transfers issued an iteration ago)
+      constexpr bool CV = FP8 && HAS_QK;
+      if (first) pv<true, PREP, HAS_QK, CV>(o, f.pf, k - 1, cb, ysend, cp, cx, da, next, L, true);
+      else pv<false, PREP, HAS_QK, CV>(o, f.pf, k - 1, cb, ysend, cp, cx, da, next, L, true);
       // index lists: the next bundle's addresses, once this bundle's transfers have read the table
       if constexpr (PREP && SPARSE) prepare(cb, L);
       if constexpr (EPI) {  // the split's last step: normalise and store its rows
         lds_barrier();  // every wave is done reading slot k - 1: it stages the epilogue
-        epilogue(cbase + cs.ci, cs.g, desc(cs.ci, D_NSPLIT), (uint32_t)((k - 1) & (NS - 1)) * kSlot, o, f, L, pin);
+        epilogue(cbase + cs.ci, cs.g, desc(cs.ci, D_NSPLIT), slot_off(k - 1), o, f, L, pin);
       }
     } else {
       // no PV: the transfers placed among the PV MFMAs go out here
 #pragma unroll
       for (int sl = 4 * KS; sl < kSlots; ++sl) side_dma<HAS_QK>(sl, ysend, cp, cx, next, da, L);
       if constexpr (PREP && SPARSE) prepare(cb, L);
+      // fp8 rows: bundle k + 1, landed (the first step of a split: the prologue or the previous
+      // split's epilogue waited for every load)
+      if constexpr (FP8 && HAS_QK) convert_all(k + 1, L);
     }
     if constexpr (PREP) {
       if constexpr (!SPARSE) dn = dense_rows(cb);
@@ -2092,6 +2148,7 @@ struct Tile128 {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qr[nt][ks]));  // Q^T has landed
     asm volatile("" : "+v"(f.sink[0]), "+v"(f.sink[1]));
+    if constexpr (FP8) convert_all(0, L0);  // published by the first iteration's barrier
 
     f32x4 o[32][2];  // O^T: [output column tile][row tile], in accumulation registers
     f32x4 sold[2][2];
