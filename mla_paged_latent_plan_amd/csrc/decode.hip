@@ -1454,10 +1454,13 @@ struct Tile128 {
   int wave, mt;
   int num_pages32;  // page count, clamped to the int range (32-bit compares stay scalar)
   int nc, T;  // splits and steps of the current chunk
+  int tok_lo, tok_hi;  // dense rows: the first and last query token among the wave's rows
 
   __device__ Tile128(const DecodeArgs& args, lds_ptr base, int tile) : a(args), sm(base), mt(tile) {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     num_pages32 = (int)min(a.num_pages, (int64_t)0x7fffffff);
+    tok_lo = min(mt * 128 + 32 * wave, a.R - 1) / a.H;
+    tok_hi = min(mt * 128 + 32 * wave + 31, a.R - 1) / a.H;
   }
 
   // The lane index, read from the hardware each time it is asked for: addresses derived from it
@@ -1802,8 +1805,16 @@ struct Tile128 {
     const int ln = L.ln;
     const int nl = ln & 15, gl = ln >> 4;
     const uint32_t vmask = sparse ? *reinterpret_cast<const LDS_AS uint32_t*>(sm + kMOff + 4 * (x & 7)) : ~0u;
-    const bool dense_mask = !sparse && (a.causal || a.window > 0);
-    const bool need = sparse ? (vmask != ~0u) : (kRows * (c.t + 1) > c.n || dense_mask);
+    bool need;
+    if (sparse) {
+      need = vmask != ~0u;
+    } else {
+      // a whole step of the group's rows inside every query row's causal / window range needs none
+      const int p0 = c.j0 + kRows * c.t, base = c.L - a.Sq;
+      const bool in_c = !a.causal || p0 + kRows - 1 <= base + tok_lo;
+      const bool in_w = a.window <= 0 || p0 >= base + tok_hi - a.window + 1;
+      need = kRows * (c.t + 1) > c.n || !(in_c && in_w);
+    }
     if (!need) return;
     if (sparse) {
       const uint32_t vm = vmask >> (4 * gl);
