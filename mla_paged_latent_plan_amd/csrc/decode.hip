@@ -1809,11 +1809,14 @@ struct Tile128 {
     if (sparse) {
       need = vmask != ~0u;
     } else {
-      // a whole step of the group's rows inside every query row's causal / window range needs none
-      const int p0 = c.j0 + kRows * c.t, base = c.L - a.Sq;
-      const bool in_c = !a.causal || p0 + kRows - 1 <= base + tok_lo;
-      const bool in_w = a.window <= 0 || p0 >= base + tok_hi - a.window + 1;
-      need = kRows * (c.t + 1) > c.n || !(in_c && in_w);
+      need = kRows * (c.t + 1) > c.n;  // past the group's rows
+      if (!need && (a.causal || a.window > 0)) {
+        // a whole step inside every query row's causal / window range needs no mask
+        const int p0 = c.j0 + kRows * c.t, base = c.L - a.Sq;
+        const bool in_c = !a.causal || p0 + kRows - 1 <= base + tok_lo;
+        const bool in_w = a.window <= 0 || p0 >= base + tok_hi - a.window + 1;
+        need = !(in_c && in_w);
+      }
     }
     if (!need) return;
     if (sparse) {
