@@ -1443,11 +1443,33 @@ struct Tile128 {
     bool up[2];
     bf16x8 pf[2];  // P^T of the step
   };
-  // Per-iteration lane constants (one read of the lane index per step).
+  // Lane constants, worked out once per chunk: the step loop issues one wave's every instruction,
+  // and a VALU instruction costs the step about as much as it takes to issue, so the per-lane
+  // parts of the operand and transfer addresses are not recomputed each step.
   struct Lane {
     int ln;        // lane
     uint32_t v16;  // 16 * lane: the lane's byte offset in a 1 KB transfer
+    uint32_t kr;   // K^T operand, RoPE region: nl * 128 + 16 (gl ^ swz_b(nl)) (chunk 4 + gl: ^ 64)
+    uint32_t irb;  // RoPE transfer: row (lane >> 3) * row bytes + the lane's byte offset in that row
+    // derived on use
+    __device__ __forceinline__ uint32_t kq() const { return (uint32_t)((ln & 15) * kRowStrideA + 16 * (ln >> 4)); }
+    __device__ __forceinline__ uint32_t vq() const {
+      return (uint32_t)((4 * (ln >> 4) + ((ln & 15) >> 2)) * kRowStrideA + 8 * (ln & 3));
+    }
+    __device__ __forceinline__ int i2() const { return ln >> 3; }
+    __device__ __forceinline__ uint32_t c16() const { return v16 ^ (uint32_t)(128 * (ln >> 5)) ^ (v16 & 512u); }
   };
+  __device__ __forceinline__ Lane make_lane() const {
+    Lane L;
+    L.ln = lane_id();
+    L.v16 = 16u * (uint32_t)L.ln;
+    const int nl = L.ln & 15, gl = L.ln >> 4;
+    L.kr = (uint32_t)(nl * 128 + 16 * (gl ^ swz_b(nl)));
+    const int i2 = L.ln >> 3;
+    const int ch = (L.ln & 7) ^ ((HAS_B || !FP8) ? swz_b(8 * wave + i2) : 0);
+    L.irb = (uint32_t)i2 * (uint32_t)a.row_bytes + (uint32_t)((FP8 ? kNope : 1024) + 16 * ch);
+    return L;
+  }
 
   const DecodeArgs& a;
   lds_ptr sm;
@@ -1619,6 +1641,14 @@ struct Tile128 {
     const uint64_t addr = (i < r.isplit) ? on0 : on1;
     return ((i < r.nvalid) ? addr : (uint64_t)(uintptr_t)a.zero_row) + off;
   }
+  // The RoPE transfer's source for each lane: row L.i2 of the bundle + L.roff, or the zero row + L.roff.
+  __device__ __forceinline__ uint64_t drow_lane(const DAddr& r, const Lane& L) const {
+    const uint64_t b1m = r.b1 - (uint64_t)(uint32_t)(r.isplit * (int)a.row_bytes);  // b1m + i rb: row i >= isplit
+    const int i2 = L.i2();
+    const uint64_t base = (i2 < r.isplit) ? r.b0 : b1m;
+    const uint64_t zero = (uint64_t)(uintptr_t)a.zero_row - (uint64_t)(uint32_t)((uint32_t)i2 * (uint32_t)a.row_bytes);
+    return ((i2 < r.nvalid) ? base : zero) + (uint64_t)L.irb;
+  }
   // Address of row i of step c, or the zero row (then *ok is false).
   __device__ __forceinline__ uint64_t row_addr(Cur c, int i, int j, int page, bool* ok) const {
     const int k = kRows * c.t + 8 * wave + i;
@@ -1656,13 +1686,10 @@ struct Tile128 {
       const int ln = L.ln;
       if (s < 4) {  // e4m3 bytes of rows 2s and 2s + 1: lanes 0-31 and 32-63, chunks swizzled
         const uint64_t r0 = drow(d, 2 * s, 0), r1 = drow(d, 2 * s + 1, 0);
-        const int chunk = (ln & 31) ^ swz_ring(2 * s + (ln >> 5));
-        const uint64_t src = (ln < 32 ? r0 : r1) + (uint64_t)(16 * chunk);
+        const uint64_t src = (ln < 32 ? r0 : r1) + (uint64_t)(L.c16() ^ (16u * (uint32_t)s));
         dma_x4<kRowsNT>(reinterpret_cast<const void*>((uintptr_t)src), lds_addr(sm + re + (8 * wave + 2 * s) * 512));
       } else if (s == 4) {  // RoPE tails: 16 bytes per lane, row ln >> 3 (chunks swizzled for QK^T)
-        const int i2 = ln >> 3;
-        const int ch = HAS_B ? ((ln & 7) ^ swz_b(8 * wave + i2)) : (ln & 7);
-        const uint64_t src = drow(d, i2, (uint32_t)kNope + 16u * (uint32_t)ch);
+        const uint64_t src = drow_lane(d, L);
         dma_x4<kRowsNT>(reinterpret_cast<const void*>((uintptr_t)src), lds_addr(sm + re + kRingRope + wave * 1024));
       } else if (s == 5) {  // scale bytes: one dword per lane, lanes 0-15
         const uint64_t src = drow_sc(d, (ln >> 1) & 7) + 4u * (uint32_t)(ln & 1);
@@ -1676,9 +1703,7 @@ struct Tile128 {
         dma_x4s<kRowsNT>(L.v16, drow(d, s, 0), lds_addr(sm + sa + (8 * wave + s) * kRowStrideA));
       } else if (s == 8) {
         if constexpr (HAS_B) {
-          const int ln = L.ln;
-          const int i2 = ln >> 3;
-          const uint64_t rope = drow(d, i2, 1024 + 16 * ((ln & 7) ^ swz_b(8 * wave + i2)));
+          const uint64_t rope = drow_lane(d, L);
           dma_x4<kRowsNT>(reinterpret_cast<const void*>((uintptr_t)rope), lds_addr(sm + sa + kSlotA + wave * 1024));
         }
       }
@@ -1861,24 +1886,37 @@ struct Tile128 {
   // reductions over the four lane groups, 8-13 the reference updates, 14-29 the exponentials and
   // sums (one value each), 30 the row sums.
   static constexpr int kSoftStages = 31;
+  // Maxima of scores as single instructions: fmaxf would first quiet each operand that the compiler
+  // cannot prove canonical (MFMA results from inline assembly, permlane results), one instruction
+  // each. The scores are never NaN (finite inputs, -inf where masked).
+  __device__ __forceinline__ static float max3_raw(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+  }
+  __device__ __forceinline__ static float max_raw(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+  }
   __device__ __forceinline__ void soft_stage(int st, Soft& f, const f32x4 (&s)[2][2]) const {
     if (st < 4) {
       const int nt = st >> 1;
       if ((st & 1) == 0) {
-        f.part[nt] = fmaxf(fmaxf(s[0][nt][0], s[0][nt][1]), s[0][nt][2]);
-        f.mx[nt] = fmaxf(fmaxf(s[0][nt][3], s[1][nt][0]), s[1][nt][1]);
+        f.part[nt] = max3_raw(s[0][nt][0], s[0][nt][1], s[0][nt][2]);
+        f.mx[nt] = max3_raw(s[0][nt][3], s[1][nt][0], s[1][nt][1]);
       } else {
-        f.part[nt] = fmaxf(fmaxf(s[1][nt][2], s[1][nt][3]), f.part[nt]);
-        f.mx[nt] = fmaxf(f.mx[nt], f.part[nt]);
+        f.part[nt] = max3_raw(s[1][nt][2], s[1][nt][3], f.part[nt]);
+        f.mx[nt] = max_raw(f.mx[nt], f.part[nt]);
       }
     } else if (st < 6) {
       const int nt = st - 4;
       const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(f.mx[nt]), __float_as_uint(f.mx[nt]), false, false);
-      f.mx[nt] = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+      f.mx[nt] = max_raw(__uint_as_float(p[0]), __uint_as_float(p[1]));
     } else if (st < 8) {
       const int nt = st - 6;
       const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(f.mx[nt]), __float_as_uint(f.mx[nt]), false, false);
-      f.mx[nt] = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+      f.mx[nt] = max_raw(__uint_as_float(p[0]), __uint_as_float(p[1]));
     } else if (st < 14) {
       const int nt = (st - 8) / 3, sub = (st - 8) % 3;
       if (sub == 0) {
@@ -1891,12 +1929,11 @@ struct Tile128 {
         f.m_ref[nt] = f.up[nt] ? f.mnew[nt] : f.m_ref[nt];
         f.l_acc[nt] *= f.alpha[nt];
         f.mu[nt] = (f.m_ref[nt] == kNegInf) ? 0.f : f.m_ref[nt];
-        f.lsum[nt] = 0.f;
       }
     } else if (st < 30) {
       const int v = st - 14, nt = v & 1, kt = (v >> 1) >> 2, e = (v >> 1) & 3;
       const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][nt][e], a.scale_log2, -f.mu[nt]));
-      f.lsum[nt] += pv;
+      f.lsum[nt] = (v < 2) ? pv : f.lsum[nt] + pv;  // the first term starts the sum
       f.pf[nt][kt * 4 + e] = (__bf16)pv;
     } else if (st == 30) {
 #pragma unroll
@@ -1934,15 +1971,13 @@ struct Tile128 {
   __device__ __forceinline__ void qk(f32x4 (&sacc)[2][2], const bf16x8 (&qr)[2][KS], int x, Soft& f,
                                     const f32x4 (&sold)[2][2], int y, Cur cp, Cur cx, const DAddr& d,
                                     uint64_t& next, const Lane& L) const {
-    const int nl = L.ln & 15, gl = L.ln >> 4;
     const uint32_t sa = slot_off(x);
     const uint32_t sb = FP8 ? ring_off(x) + kRingRope : sa + kSlotA;
-    const uint32_t kaddr = sa + nl * kRowStrideA + 16 * gl;
+    const uint32_t kaddr = sa + L.kq();
     auto k_op = [&](int kt, int ks) -> bf16x8 {
       if (ks < 16) return lds_read_b128(sm, kaddr + 16 * kt * kRowStrideA + 64 * ks);
-      const int row = 16 * kt + nl;
-      const int c = (4 * (ks - 16) + gl) ^ swz_b(row);
-      return lds_read_b128(sm, sb + row * 128 + 16 * c);
+      // row 16 kt + nl, chunk (4 (ks - 16) + gl) ^ swz_b(row) (swz_b is the same for both kt)
+      return lds_read_b128(sm, sb + (L.kr ^ (64u * (uint32_t)(ks - 16))) + 2048 * kt);
     };
     constexpr int D = 3;  // operand steps in flight
     bf16x8 ka[D][2];
@@ -1978,13 +2013,12 @@ struct Tile128 {
   template <bool FIRST, bool PREP, bool SEND, bool CV>
   __device__ __forceinline__ void pv(f32x4 (&o)[32][2], const bf16x8 (&pf)[2], int x, Cur c, int y, Cur cp,
                                     Cur cx, const DAddr& d, uint64_t& next, const Lane& L, bool wait) const {
-    const int nl = L.ln & 15, gl = L.ln >> 4;
     const uint32_t sa = slot_off(x);
     Cv cv;
     if constexpr (CV) {
       if (wait) wait_landed();
     }
-    const uint32_t vbase = sa + (4 * gl + (nl >> 2)) * kRowStrideA + 8 * (nl & 3);
+    const uint32_t vbase = sa + L.vq();
     auto v_op = [&](int ct) -> bf16x8 {
       const uint32_t ad = vbase + 32 * ct;
       const bf16x4 v0 = lds_read_tr(sm, ad);
@@ -2040,16 +2074,20 @@ struct Tile128 {
   template <bool HAS_QK, bool HAS_PV, bool EPI, bool PREP, class Pin = NoPin>
   __device__ __forceinline__ void iteration(int k, bf16x8 (&qr)[2][KS], f32x4 (&o)[32][2], f32x4 (&sold)[2][2],
                                             Soft& f, Cur& cq, Cur& cs, Cur& cb, Cur& cp, Cur& cx, DRows& dn,
-                                            int cbase, bool wait, const Pin& pin = Pin()) {
+                                            int cbase, bool wait, const Lane& L0, const Pin& pin = Pin()) {
     if constexpr (HAS_QK && !FP8) {
       if (wait) wait_landed();
     }
     // rows of step k visible (fp8 rows: converted in the previous iteration); every wave is done with
     // steps k - 2 (PV) and k - 1 (QK)
     lds_barrier();
-    Lane L;
-    L.ln = lane_id();
-    L.v16 = 16u * (uint32_t)L.ln;
+    // The lane index is read again from the hardware (not held across the step); with fp8 rows, whose
+    // conversion needs more registers, the other lane constants are worked out again as well.
+    Lane L = FP8 ? make_lane() : L0;
+    if constexpr (!FP8) {
+      L.ln = lane_id();
+      L.v16 = 16u * (uint32_t)L.ln;
+    }
     DAddr da;
     if constexpr (HAS_QK && !SPARSE) da = dense_addr(dn);  // bundle k + 2 (entries loaded a step ago)
     if constexpr (HAS_PV) {
@@ -2115,14 +2153,10 @@ struct Tile128 {
     // once (their one wait follows the transfers). -----------------------------------------------
     bf16x8 qr[2][KS];
     load_q(qr, c0.g);
+    const Lane L0 = make_lane();
     Soft f;
     soft_reset(f);
-    {
-      Lane Ls;
-      Ls.ln = lane_id();
-      Ls.v16 = 0;
-      load_sink(f.sink, desc(c0.ci, D_NSPLIT), Ls);
-    }
+    load_sink(f.sink, desc(c0.ci, D_NSPLIT), L0);
     if (sparse) {
 #pragma unroll 1
       for (int i = 0; i < 6; ++i) {
@@ -2138,9 +2172,6 @@ struct Tile128 {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // entries in LDS before prepare reads them
     }
     DRows dn;
-    Lane L0;
-    L0.ln = lane_id();
-    L0.v16 = 16u * (uint32_t)L0.ln;
 #pragma unroll 1
     for (int i = 0; i < 2; ++i) {
       DAddr d0;
@@ -2174,9 +2205,10 @@ struct Tile128 {
 #pragma unroll 1
     for (int ci = 0; ci < nc; ++ci) {
       const int k0 = k, kend = k + (cq.qend - cq.q0);
-      iteration<true, false, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, false);
+      iteration<true, false, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, false, L0);
 #pragma unroll 1
-      for (++k; k < kend; ++k) iteration<true, true, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, k > k0 + 1);
+      for (++k; k < kend; ++k)
+        iteration<true, true, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, k > k0 + 1, L0);
       // Q^T of the next split (cq: its first step) is requested before this split's last PV and
       // epilogue, which no longer need the registers, so it lands while they run. The epilogue waits
       // for it (and so for every load issued so far) before its stores, and the next split's sink
@@ -2190,13 +2222,8 @@ struct Tile128 {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qr[nt][ks]));
       };
-      iteration<false, true, true, false>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, false, pin);
-      if (ci + 1 < nc) {
-        Lane Ls;
-        Ls.ln = lane_id();
-        Ls.v16 = 0;
-        load_sink(f.sink, desc(cq.ci, D_NSPLIT), Ls);
-      }
+      iteration<false, true, true, false>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, false, L0, pin);
+      if (ci + 1 < nc) load_sink(f.sink, desc(cq.ci, D_NSPLIT), L0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the epilogue's stores, zero-row bundles past the end
   }
