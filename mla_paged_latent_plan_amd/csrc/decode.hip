@@ -2073,6 +2073,7 @@ struct Tile128 {
   };
   template <bool HAS_QK, bool HAS_PV, bool EPI, bool PREP, class Pin = NoPin>
   __device__ __forceinline__ void iteration(int k, bf16x8 (&qr)[2][KS], f32x4 (&o)[32][2], f32x4 (&sold)[2][2],
+                                            f32x4 (&snew)[2][2],
                                             Soft& f, Cur& cq, Cur& cs, Cur& cb, Cur& cp, Cur& cx, DRows& dn,
                                             int cbase, bool wait, const Lane& L0, const Pin& pin = Pin()) {
     if constexpr (HAS_QK && !FP8) {
@@ -2097,7 +2098,6 @@ struct Tile128 {
     const int ysend = cb.y - 1;  // bundle k + 2
     uint64_t next = 0;
     if constexpr (HAS_QK && SPARSE) next = rb_read(0);
-    f32x4 snew[2][2];
     if constexpr (HAS_QK) {
       qk<HAS_PV, true>(snew, qr, k, f, sold, ysend, cp, cx, da, next, L);
     } else {
@@ -2135,11 +2135,7 @@ struct Tile128 {
         cx = cur_next(cx);
       }
     }
-    if constexpr (HAS_QK) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sold[kt][nt] = snew[kt][nt];
+    if constexpr (HAS_QK) {  // the caller swaps the roles of sold and snew for the next step
       cs = cq;
       cq = cur_next(cq);
     }
@@ -2196,7 +2192,7 @@ struct Tile128 {
     if constexpr (FP8) convert_all(0, L0);  // published by the first iteration's barrier
 
     f32x4 o[32][2];  // O^T: [output column tile][row tile], in accumulation registers
-    f32x4 sold[2][2];
+    f32x4 sa_[2][2], sb_[2][2];  // scores of a step, the two arrays taking turns as the new and old ones
     Cur cq = c0, cs = c0;
     // One pipelined loop per split. A split's Q^T is loaded between loops, so no loop holds a load
     // whose wait the compiler would place among the MFMAs (such a wait would also hold for the row
@@ -2205,10 +2201,21 @@ struct Tile128 {
 #pragma unroll 1
     for (int ci = 0; ci < nc; ++ci) {
       const int k0 = k, kend = k + (cq.qend - cq.q0);
-      iteration<true, false, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, false, L0);
+      iteration<true, false, false, true>(k, qr, o, sb_, sa_, f, cq, cs, cb, cp, cx, dn, cb0, false, L0);
+      // two steps per trip, so that the score arrays swap roles without copies
 #pragma unroll 1
-      for (++k; k < kend; ++k)
-        iteration<true, true, false, true>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, k > k0 + 1, L0);
+      for (++k; k + 1 < kend; k += 2) {
+        iteration<true, true, false, true>(k, qr, o, sa_, sb_, f, cq, cs, cb, cp, cx, dn, cb0, k > k0 + 1, L0);
+        iteration<true, true, false, true>(k + 1, qr, o, sb_, sa_, f, cq, cs, cb, cp, cx, dn, cb0, true, L0);
+      }
+      if (k < kend) {
+        iteration<true, true, false, true>(k, qr, o, sa_, sb_, f, cq, cs, cb, cp, cx, dn, cb0, k > k0 + 1, L0);
+        ++k;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) sa_[kt][nt] = sb_[kt][nt];
+      }
       // Q^T of the next split (cq: its first step) is requested before this split's last PV and
       // epilogue, which no longer need the registers, so it lands while they run. The epilogue waits
       // for it (and so for every load issued so far) before its stores, and the next split's sink
@@ -2222,7 +2229,7 @@ struct Tile128 {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qr[nt][ks]));
       };
-      iteration<false, true, true, false>(k, qr, o, sold, f, cq, cs, cb, cp, cx, dn, cb0, false, L0, pin);
+      iteration<false, true, true, false>(k, qr, o, sa_, sb_, f, cq, cs, cb, cp, cx, dn, cb0, false, L0, pin);
       if (ci + 1 < nc) load_sink(f.sink, desc(cq.ci, D_NSPLIT), L0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the epilogue's stores, zero-row bundles past the end
