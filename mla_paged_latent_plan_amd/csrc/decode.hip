@@ -1439,7 +1439,7 @@ struct Tile128 {
   struct Soft {
     float m_ref[2], l_acc[2], m_top[2];  // per row tile: reference maximum, sum, true maximum
     float alpha[2], mu[2], lsum[2], mx[2], mnew[2], part[2];
-    float sink[2];  // sink logits of the split's rows (-inf: none)
+    float sink[2];   // sink logits of the split's rows (-inf: none)
     bool up[2];
     bf16x8 pf[2];  // P^T of the step
   };
@@ -1882,9 +1882,9 @@ struct Tile128 {
 
   // Softmax of the wave's rows (base 2, lazy reference maximum) in micro-stages of at most two VALU
   // instructions or one exponential, so the QK^T loop of the next step can run one between each pair
-  // of MFMAs (one wave hides about two VALU instructions under an MFMA): 0-3 row maxima, 4-7 their
-  // reductions over the four lane groups, 8-13 the reference updates, 14-29 the exponentials and
-  // sums (one value each), 30 the row sums.
+  // of MFMAs (one wave hides about two VALU instructions under an MFMA): 0-3 row maxima, 4-6 their
+  // reductions over the four lane groups (both row tiles through one permlane sequence), 8-13 the
+  // reference updates, 14-29 the exponentials and sums (one value each), 30 the row sums.
   static constexpr int kSoftStages = 31;
   // Maxima of scores as single instructions: fmaxf would first quiet each operand that the compiler
   // cannot prove canonical (MFMA results from inline assembly, permlane results), one instruction
@@ -1909,20 +1909,25 @@ struct Tile128 {
         f.part[nt] = max3_raw(s[1][nt][2], s[1][nt][3], f.part[nt]);
         f.mx[nt] = max_raw(f.mx[nt], f.part[nt]);
       }
-    } else if (st < 6) {
-      const int nt = st - 4;
-      const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(f.mx[nt]), __float_as_uint(f.mx[nt]), false, false);
-      f.mx[nt] = max_raw(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    } else if (st < 8) {
-      const int nt = st - 6;
-      const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(f.mx[nt]), __float_as_uint(f.mx[nt]), false, false);
-      f.mx[nt] = max_raw(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    } else if (st < 14) {
+    } else if (st == 4) {
+      // lane groups (rows of 16 lanes) r0..r3 hold partial maxima a (tile 0) and b (tile 1): swapping
+      // a's odd rows with b's even rows leaves max(a.r0, a.r1), max(b.r0, b.r1), max(a.r2, a.r3),
+      // max(b.r2, b.r3) in rows 0-3
+      const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(f.mx[0]), __float_as_uint(f.mx[1]), false, false);
+      f.mx[0] = max_raw(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    } else if (st == 5) {  // rows 0 and 2: tile 0's maximum; rows 1 and 3: tile 1's
+      const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(f.mx[0]), __float_as_uint(f.mx[0]), false, false);
+      f.mx[0] = max_raw(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    } else if (st == 6) {  // the even rows' value to every row, and the odd rows'
+      const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(f.mx[0]), __float_as_uint(f.mx[0]), false, false);
+      f.mx[0] = __uint_as_float(p[0]);
+      f.mx[1] = __uint_as_float(p[1]);
+    } else if (st >= 8 && st < 14) {
       const int nt = (st - 8) / 3, sub = (st - 8) % 3;
       if (sub == 0) {
         f.mnew[nt] = f.mx[nt] * a.scale_log2;  // -inf stays -inf (scale > 0)
         f.up[nt] = f.mnew[nt] > f.m_ref[nt] + kTau;
-        if constexpr (MAXL) f.m_top[nt] = fmaxf(f.m_top[nt], f.mnew[nt]);
+        if constexpr (MAXL) f.m_top[nt] = max_raw(f.m_top[nt], f.mnew[nt]);
       } else if (sub == 1) {
         f.alpha[nt] = f.up[nt] ? __builtin_amdgcn_exp2f(f.m_ref[nt] - f.mnew[nt]) : 1.f;  // m_ref = -inf -> 0
       } else {
@@ -1930,7 +1935,7 @@ struct Tile128 {
         f.l_acc[nt] *= f.alpha[nt];
         f.mu[nt] = (f.m_ref[nt] == kNegInf) ? 0.f : f.m_ref[nt];
       }
-    } else if (st < 30) {
+    } else if (st >= 14 && st < 30) {
       const int v = st - 14, nt = v & 1, kt = (v >> 1) >> 2, e = (v >> 1) & 3;
       const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][nt][e], a.scale_log2, -f.mu[nt]));
       f.lsum[nt] = (v < 2) ? pv : f.lsum[nt] + pv;  // the first term starts the sum
