@@ -1643,6 +1643,7 @@ struct Tile128 {
   }
   // The RoPE transfer's source for each lane: row L.i2 of the bundle + L.roff, or the zero row + L.roff.
   __device__ __forceinline__ uint64_t drow_lane(const DAddr& r, const Lane& L) const {
+    if (r.isplit >= 8 && r.nvalid >= 8) return r.b0 + (uint64_t)L.irb;  // the usual case: one page, all valid
     const uint64_t b1m = r.b1 - (uint64_t)(uint32_t)(r.isplit * (int)a.row_bytes);  // b1m + i rb: row i >= isplit
     const int i2 = L.i2();
     const uint64_t base = (i2 < r.isplit) ? r.b0 : b1m;
@@ -1685,8 +1686,15 @@ struct Tile128 {
       const uint32_t re = ring_off(y);
       const int ln = L.ln;
       if (s < 4) {  // e4m3 bytes of rows 2s and 2s + 1: lanes 0-31 and 32-63, chunks swizzled
-        const uint64_t r0 = drow(d, 2 * s, 0), r1 = drow(d, 2 * s + 1, 0);
-        const uint64_t src = (ln < 32 ? r0 : r1) + (uint64_t)(L.c16() ^ (16u * (uint32_t)s));
+        const uint32_t co = L.c16() ^ (16u * (uint32_t)s);
+        uint64_t src;
+        if (d.isplit >= 8 && d.nvalid >= 8) {  // the usual case: one page, all valid
+          const uint32_t hr = (uint32_t)(ln >> 5) * (uint32_t)a.row_bytes;
+          src = d.b0 + (uint64_t)(uint32_t)(2 * s * (int)a.row_bytes) + (uint64_t)(hr + co);
+        } else {
+          const uint64_t r0 = drow(d, 2 * s, 0), r1 = drow(d, 2 * s + 1, 0);
+          src = (ln < 32 ? r0 : r1) + (uint64_t)co;
+        }
         dma_x4<kRowsNT>(reinterpret_cast<const void*>((uintptr_t)src), lds_addr(sm + re + (8 * wave + 2 * s) * 512));
       } else if (s == 4) {  // RoPE tails: 16 bytes per lane, row ln >> 3 (chunks swizzled for QK^T)
         const uint64_t src = drow_lane(d, L);
