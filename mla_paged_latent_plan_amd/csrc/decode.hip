@@ -1760,15 +1760,20 @@ struct Tile128 {
     u32x4 w[4];   // the group's e4m3 bytes
     bf16x8 x;     // the write in progress
     u32x4 rp;     // 512-wide rows, group 7: the RoPE chunk of the write in progress
+    uint32_t src; // ring entry + the lane's first source chunk (chunk i: ^ 16 i; i only flips the
+                  // two low bits of the swizzled chunk index)
+    uint32_t dst; // bf16 slot + the lane's row and group
   };
   __device__ __forceinline__ void cv_stage(int st, Cv& c, int x, const Lane& L) const {
     const int ln = L.ln, r = 8 * wave + (ln & 7), gi = ln >> 3;
     const uint32_t re = ring_off(x);
     if (st == 0) {
       c.sw = *reinterpret_cast<const LDS_AS uint32_t*>(sm + re + kRingSc + 8 * r + (gi & 4));
+      c.src = re + 512u * (uint32_t)r + 16u * (uint32_t)((4 * gi) ^ swz_ring(r));
+      c.dst = slot_off(x) + (uint32_t)r * kRowStrideA + 128u * (uint32_t)gi;
     } else if (st <= 4) {
       const int i = st - 1;
-      c.w[i] = *reinterpret_cast<const LDS_AS u32x4*>(sm + re + 512u * (uint32_t)r + 16 * ((4 * gi + i) ^ swz_ring(r)));
+      c.w[i] = *reinterpret_cast<const LDS_AS u32x4*>(sm + (c.src ^ (16u * (uint32_t)i)));
     } else if (st == 5) {
       c.sc = ue8m0_f32((c.sw >> (8 * (gi & 3))) & 0xFFu);
     } else {
@@ -1797,8 +1802,7 @@ struct Tile128 {
       } else {
         u32x4 v = __builtin_bit_cast(u32x4, c.x);
         if constexpr (!HAS_B) v = (gi < NG) ? v : c.rp;
-        const uint32_t dst = slot_off(x) + (uint32_t)r * kRowStrideA + 128u * (uint32_t)gi + 32u * (uint32_t)i + (hi ? 16u : 0u);
-        *reinterpret_cast<LDS_AS u32x4*>(sm + dst) = v;
+        *reinterpret_cast<LDS_AS u32x4*>(sm + c.dst + 32u * (uint32_t)i + (hi ? 16u : 0u)) = v;
       }
     }
   }
