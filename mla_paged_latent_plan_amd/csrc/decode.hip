@@ -1451,11 +1451,10 @@ struct Tile128 {
     uint32_t v16;  // 16 * lane: the lane's byte offset in a 1 KB transfer
     uint32_t kr;   // K^T operand, RoPE region: nl * 128 + 16 (gl ^ swz_b(nl)) (chunk 4 + gl: ^ 64)
     uint32_t irb;  // RoPE transfer: row (lane >> 3) * row bytes + the lane's byte offset in that row
-    // derived on use
-    __device__ __forceinline__ uint32_t kq() const { return (uint32_t)((ln & 15) * kRowStrideA + 16 * (ln >> 4)); }
-    __device__ __forceinline__ uint32_t vq() const {
-      return (uint32_t)((4 * (ln >> 4) + ((ln & 15) >> 2)) * kRowStrideA + 8 * (ln & 3));
-    }
+    uint32_t kq_;  // K^T operand (rows nl, nl + 16 of a slot): nl * row stride + 16 gl
+    uint32_t vq_;  // V^T operand: row 4 gl + (nl >> 2) = lane >> 2, column 4 (nl & 3)
+    __device__ __forceinline__ uint32_t kq() const { return kq_; }
+    __device__ __forceinline__ uint32_t vq() const { return vq_; }
     __device__ __forceinline__ int i2() const { return ln >> 3; }
     __device__ __forceinline__ uint32_t c16() const { return v16 ^ (uint32_t)(128 * (ln >> 5)) ^ (v16 & 512u); }
   };
@@ -1465,6 +1464,8 @@ struct Tile128 {
     L.v16 = 16u * (uint32_t)L.ln;
     const int nl = L.ln & 15, gl = L.ln >> 4;
     L.kr = (uint32_t)(nl * 128 + 16 * (gl ^ swz_b(nl)));
+    L.kq_ = (uint32_t)(nl * kRowStrideA + 16 * gl);
+    L.vq_ = (uint32_t)((L.ln >> 2) * kRowStrideA + 8 * (L.ln & 3));
     const int i2 = L.ln >> 3;
     const int ch = (L.ln & 7) ^ ((HAS_B || !FP8) ? swz_b(8 * wave + i2) : 0);
     L.irb = (uint32_t)i2 * (uint32_t)a.row_bytes + (uint32_t)((FP8 ? kNope : 1024) + 16 * ch);
@@ -1874,8 +1875,9 @@ struct Tile128 {
       for (int nt = 0; nt < 2; ++nt) {
         // the query's position pos = L - Sq + token (token = row / H), relative to the step offset;
         // rows past R take row R - 1's (their Q^T is row R - 1's too)
-        const int rel = c.L - a.Sq + min(mt * 128 + 32 * wave + 16 * nt + nl, a.R - 1) / a.H - c.j0 - kbase;
-        hi[nt] = a.causal ? rel : (1 << 30);
+        const uint32_t row = (uint32_t)min(mt * 128 + 32 * wave + 16 * nt + nl, a.R - 1);
+        const int rel = c.L - a.Sq + (int)(row / (uint32_t)a.H) - c.j0 - kbase;
+        hi[nt] = min(a.causal ? rel : (1 << 30), nrem - 1);  // the group's rows end at nrem
         lo[nt] = a.window > 0 ? rel - a.window + 1 : -(1 << 30);
       }
 #pragma unroll
@@ -1885,7 +1887,7 @@ struct Tile128 {
           const int cc = 16 * kt + e;
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
-            const bool ok = (cc < nrem) & (cc <= hi[nt]) & (cc >= lo[nt]);
+            const bool ok = (cc <= hi[nt]) & (cc >= lo[nt]);
             s[kt][nt][e] = ok ? s[kt][nt][e] : kNegInf;
           }
         }
