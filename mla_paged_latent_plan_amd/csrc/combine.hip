@@ -11,7 +11,9 @@
 //
 // Launch: workgroups of 256 threads over (4 query rows, group); 64 threads per row, each owning 8
 // consecutive columns, so bf16 partial rows are read as contiguous 1 KB lines. Lane i reads the LSE
-// of split i (per chunk of 64 splits); eight splits' rows are loaded before they are accumulated.
+// of split i (per chunk of 64 splits); seven splits' rows are loaded before they are accumulated,
+// through buffer loads (a scalar descriptor per split block, one lane offset for all), and at most
+// 64 VGPRs keep eight waves on each SIMD, so a grid of 2048 workgroups is resident at once.
 // Groups with more than one split number at most U - 1 (each straddles a unit boundary), so the
 // grid's group dimension is capped at U and a workgroup strides over groups; those with one split
 // (already final) cost it only their two split pointers.
@@ -22,7 +24,7 @@ namespace mla {
 namespace {
 
 constexpr int kRowsPerBlock = 4;
-constexpr int kDepth = 8;  // partial rows in flight per lane
+constexpr int kDepth = 7;  // partial rows in flight per lane (groups of three or more splits)
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
@@ -43,8 +45,22 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ void combine_group(const CombineArgs& a, int g, int s0, int s1);
 
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  if (!plan_matches(a.plan, a.G, a.U, a.R)) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void combine_kernel(CombineArgs a) {
+  // The split pointers of the workgroup's first four groups are requested with the plan's header
+  // words, one memory round trip for both; they are used only if the header matches.
+  const int gstep = gridDim.y;
+  int p0[4], p1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = min((int)blockIdx.y + i * gstep, a.G - 1);
+    p0[i] = a.plan[a.grp_ptr_off + g];
+    p1[i] = a.plan[a.grp_ptr_off + g + 1];
+  }
+  const bool match = plan_matches(a.plan, a.G, a.U, a.R);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" ::"s"(p0[i]), "s"(p1[i]));  // issued before the test
+  if (!match) {
 #pragma unroll 1
     // a plan of another problem: the decode skipped its work, and every output row is NaN
     for (int g = blockIdx.y; g < a.G; g += gridDim.y) {
@@ -61,33 +77,30 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
     return;
   }
-  // the split pointers of the workgroup's first four groups are requested together
-  const int gstep = gridDim.y;
-  int p0[4], p1[4];
+  // a workgroup whose groups all have one split (finished by the decode) leaves at once
+  bool work = (int)blockIdx.y + 4 * gstep < a.G;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int g = min((int)blockIdx.y + i * gstep, a.G - 1);
-    p0[i] = a.plan[a.grp_ptr_off + g];
-    p1[i] = a.plan[a.grp_ptr_off + g + 1];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int g = (int)blockIdx.y + i * gstep;
-    if (g < a.G) {
-      const int s0 = __builtin_amdgcn_readfirstlane(p0[i]), s1 = __builtin_amdgcn_readfirstlane(p1[i]);
-      if (s1 - s0 != 1) combine_group(a, g, s0, s1);
-    }
-  }
+  for (int i = 0; i < 4; ++i) work |= ((int)blockIdx.y + i * gstep < a.G) && (p1[i] - p0[i] != 1);
+  if (!work) return;
 #pragma unroll 1
-  for (int g = (int)blockIdx.y + 4 * gstep; g < a.G; g += gstep) {
-    const int s0 = __builtin_amdgcn_readfirstlane(a.plan[a.grp_ptr_off + g]);
-    const int s1 = __builtin_amdgcn_readfirstlane(a.plan[a.grp_ptr_off + g + 1]);
+  for (int i = 0, g = (int)blockIdx.y; g < a.G; ++i, g += gstep) {
+    int s0, s1;
+    if (i < 4) {
+      s0 = (i == 0) ? p0[0] : (i == 1) ? p0[1] : (i == 2) ? p0[2] : p0[3];
+      s1 = (i == 0) ? p1[0] : (i == 1) ? p1[1] : (i == 2) ? p1[2] : p1[3];
+    } else {
+      s0 = a.plan[a.grp_ptr_off + g];
+      s1 = a.plan[a.grp_ptr_off + g + 1];
+    }
+    s0 = __builtin_amdgcn_readfirstlane(s0);
+    s1 = __builtin_amdgcn_readfirstlane(s1);
     if (s1 - s0 != 1) combine_group(a, g, s0, s1);
   }
 }
 
 // The merge of group g's splits [s0, s1) for the workgroup's four rows.
 __device__ __forceinline__ void combine_group(const CombineArgs& a, int g, int s0, int s1) {
+  constexpr int D = kDepth;
   const int ns = s1 - s0;
   const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (r >= a.R) return;
@@ -106,18 +119,32 @@ __device__ __forceinline__ void combine_group(const CombineArgs& a, int g, int s
   }
 
   // The row's split weights: lane i holds split s0 + i of each 64-split chunk. The first chunk's
-  // LSEs and the first kDepth splits' rows are requested together, so a group with at most kDepth
-  // splits costs one memory round trip before its sums; larger groups then load kDepth rows at a
+  // LSEs and the first D splits' rows are requested together, so a group with at most D splits
+  // costs one memory round trip before its sums; larger groups then load D rows at a
   // time. Rows are accumulated in split order.
-  const int64_t row0 = (int64_t)r * kDv + c;
-  const uint16_t* po = a.part_o + (int64_t)s0 * a.R * kDv + row0;
-  const int64_t po_step = (int64_t)a.R * kDv;
-  // (indices past the group's last split repeat it: uniform, branch-free loads whose rows are
-  // not accumulated)
-  uint4 v[kDepth];
+  // A split's partial block is R rows of 1 KB: the row's columns sit at a lane offset below 2^32
+  // bytes in each block, and the block's address is wave-uniform (a scalar base plus that offset).
+  const uint32_t lane_off = (uint32_t)(r * kDv + c) * 2u;
+  const uint8_t* pbase = reinterpret_cast<const uint8_t*>(a.part_o) + (int64_t)s0 * a.R * kDv * 2;
+  const int64_t pstep = (int64_t)a.R * kDv * 2;
+  // buffer load of split block i: a scalar descriptor and the lane offset
+  auto ld = [&](int i) -> uint4 {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(pbase + i * pstep), (short)0, (int)pstep, 0x00020000);
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, 0, 0);
+    return uint4{w[0], w[1], w[2], w[3]};
+  };
+
+  // (indices past the group's last split repeat it: loads whose rows are not accumulated; groups
+  // of two splits, from short windows or index lists of a few blocks, skip the other five)
+  uint4 v[D];
   if (ns > 0) {
+    v[0] = ld(0);
+    v[1] = ld(min(1, ns - 1));
+    if (ns > 2) {
 #pragma unroll
-    for (int q = 0; q < kDepth; ++q) v[q] = *reinterpret_cast<const uint4*>(po + min(q, ns - 1) * po_step);
+      for (int q = 2; q < D; ++q) v[q] = ld(min(q, ns - 1));
+    }
   }
   float ls0 = (lane < ns) ? a.part_lse[(int64_t)(s0 + lane) * a.R + r] : kNegInf;
   float mx = ls0;
@@ -135,14 +162,14 @@ __device__ __forceinline__ void combine_group(const CombineArgs& a, int g, int s
       const float wl = (ls == kNegInf) ? 0.f : __expf(ls - mx);
       wsum += wl;
       const int nc = min(64, s1 - sc);
-      for (int k = 0; k < nc; k += kDepth) {
-        if (sc != s0 || k != 0) {  // the first kDepth rows are already loaded
+      for (int k = 0; k < nc; k += D) {
+        if (sc != s0 || k != 0) {  // the first D rows are already loaded
 #pragma unroll
-          for (int q = 0; q < kDepth; ++q)
-            v[q] = *reinterpret_cast<const uint4*>(po + (sc - s0 + min(k + q, nc - 1)) * po_step);
+          for (int q = 0; q < D; ++q)
+            v[q] = ld(sc - s0 + min(k + q, nc - 1));
         }
 #pragma unroll
-        for (int q = 0; q < kDepth; ++q) {
+        for (int q = 0; q < D; ++q) {
           if (k + q < nc) {
             const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k + q));
             const uint32_t u[4] = {v[q].x, v[q].y, v[q].z, v[q].w};

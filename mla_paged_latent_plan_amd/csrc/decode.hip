@@ -2380,9 +2380,8 @@ void decode_tile128_kernel(DecodeArgs a, int per) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[Tile128<DQK, MAXL, SPARSE, FP8>::LDS];
   int unit, mt;
   unit_tile_blocked(blockIdx.x, a.m_tiles, per, &unit, &mt);
-  if (unit >= a.U || !plan_matches(a.plan, a.G, a.U, a.R)) return;
-  const int s0 = a.plan[a.unit_ptr_off + unit];
-  const int s1 = a.plan[a.unit_ptr_off + unit + 1];
+  int s0, s1;
+  if (!unit_splits<!MAXL>(a, unit, &s0, &s1)) return;
   Tile128<DQK, MAXL, SPARSE, FP8> d(a, (lds_ptr)lds, mt);
   d.run_unit(s0, s1);
 }
@@ -2402,9 +2401,8 @@ void decode_spec64_kernel(DecodeArgs a) {
   const lds_ptr base = (lds_ptr)lds;
   int unit, mt;
   unit_tile(blockIdx.x, a.m_tiles, &unit, &mt);
-  if (unit >= a.U || !plan_matches(a.plan, a.G, a.U, a.R)) return;
-  const int s0 = a.plan[a.unit_ptr_off + unit];
-  const int s1 = a.plan[a.unit_ptr_off + unit + 1];
+  int s0, s1;
+  if (!unit_splits(a, unit, &s0, &s1)) return;
   Spec64<DQK, FP8> d(a, base);
   if (d.wave < 4) {
     for (int s = s0; s < s1; ++s) {
@@ -2427,9 +2425,8 @@ void decode_kernel(DecodeArgs a) {
   const int m_tiles = a.m_tiles;
   const int unit = blockIdx.x / m_tiles;
   const int mt = blockIdx.x % m_tiles;
-  if (unit >= a.U || !plan_matches(a.plan, a.G, a.U, a.R)) return;
-  const int s0 = a.plan[a.unit_ptr_off + unit];
-  const int s1 = a.plan[a.unit_ptr_off + unit + 1];
+  int s0, s1;
+  if (!unit_splits<false>(a, unit, &s0, &s1)) return;
   Decoder<C> d(a, base);
   for (int s = s0; s < s1; ++s) d.run_split(s, mt);
 }

@@ -110,6 +110,29 @@ __device__ __forceinline__ bool plan_matches(const int32_t* plan, int G, int U, 
   return magic == kPlanMagic && g == G && u == U && r == R && smax == G + U;
 }
 
+// The split range [s0, s1) of a decode work unit, requested with the plan's header words (one
+// memory round trip for both); false when the unit is past U or the plan is of another problem.
+// (Without EARLY, the range is read after the test: kernels whose scalar registers are short keep
+// the two words out of the header's round trip.)
+template <bool EARLY = true>
+__device__ __forceinline__ bool unit_splits(const DecodeArgs& a, int unit, int* s0, int* s1) {
+  if constexpr (EARLY) {
+    const int uc = min(unit, a.U - 1);
+    const int b0 = a.plan[a.unit_ptr_off + uc];
+    const int b1 = a.plan[a.unit_ptr_off + uc + 1];
+    const bool match = plan_matches(a.plan, a.G, a.U, a.R);
+    asm volatile("" ::"s"(b0), "s"(b1));  // issued before the test
+    *s0 = b0;
+    *s1 = b1;
+    return match && unit < a.U;
+  } else {
+    if (unit >= a.U || !plan_matches(a.plan, a.G, a.U, a.R)) return false;
+    *s0 = a.plan[a.unit_ptr_off + unit];
+    *s1 = a.plan[a.unit_ptr_off + unit + 1];
+    return true;
+  }
+}
+
 struct KvWriteArgs {
   const uint16_t* kv_c;  // bf16 [n][d_nope]
   const uint16_t* k_pe;  // bf16 [n][64]
