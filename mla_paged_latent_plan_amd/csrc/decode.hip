@@ -39,6 +39,21 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// Output and partial stores of the 64- and 128-row kernels as inline assembly, with device scope
+// (sc1): each write goes through the XCD's L2 to the device's coherence point as it is made, so
+// the release at the kernel's end has few dirty L2 lines left to write back before the next
+// kernel may start (about 2 us off a 110 us step; the 16-row kernel's stores are faster without
+// it). The compiler's wait-count pass does not see these stores, so it does not make later
+// register writes wait for them (with LDS-DMA transfers in flight, such a wait would also hold
+// for every transfer); nothing in a decode kernel reads what it stores. One wait state after each
+// guards the store-data hazard.
+__device__ __forceinline__ void st_global_b128(void* p, const u32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_global_b32(void* p, float v) {
+  asm volatile("global_store_dword %0, %1, off sc1\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
+}
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
@@ -789,15 +804,6 @@ __device__ __forceinline__ void mfma_sq2_cvt_last(f32x4& c0, f32x4& c1, const bf
       : "+v"(c0), "+v"(c1)
       : "v"(a0), "v"(a1), "a"(b));
 }
-// Global stores as inline assembly: the compiler's wait-count pass does not see them, so it does
-// not make later register writes wait for them (with the LDS-DMA transfers in flight, such a wait
-// would also hold for every transfer). One wait state after each guards the store-data hazard.
-__device__ __forceinline__ void st_global_b128(void* p, const u32x4& v) {
-  asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
-}
-__device__ __forceinline__ void st_global_b32(void* p, float v) {
-  asm volatile("global_store_dword %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
-}
 // An accumulator tile read into VGPRs by explicit copies: the tile stays an accumulation-register
 // value for the compiler (a plain VALU use would make it re-home the whole array).
 __device__ __forceinline__ f32x4 acc_read(const f32x4& o) {
@@ -1168,7 +1174,7 @@ struct Spec64 {
       if (r < a.R) {
         const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(sm + hrow * kStageRow + 16 * lane);
         uint16_t* dst = final_out ? a.out + ((int64_t)g * a.R + r) * kDv : a.part_o + ((int64_t)s * a.R + r) * kDv;
-        *reinterpret_cast<u32x4*>(dst + 8 * lane) = v;
+        st_global_b128(dst + 8 * lane, v);
       }
     }
   }
