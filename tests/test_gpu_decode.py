@@ -76,6 +76,13 @@ CASES = {
     "fp8_h128_sink_empty": (Spec("fp8_h128_sink_empty", batch=3, q_len=1, num_heads=128,
                                  page_size=64, kv_format="fp8", seqlens=(0, 700, 0), sink=True,
                                  sm_scale=S, seed=37), None),
+    # index lists / windows of 16+ blocks over a few groups: each group split 16-17 ways when
+    # planned on the device or on 1024 CUs (the combine's multi-batch merge, uneven last batch)
+    "sparse_wide_h16": (Spec("sparse_wide_h16", batch=2, q_len=1, num_heads=16, page_size=64,
+                             seqlens=(5000, 3000), topk=1024, sm_scale=S, seed=40), None),
+    "win_wide_sink": (Spec("win_wide_sink", batch=2, q_len=2, num_heads=16, page_size=64,
+                           seqlens=(3000, 1500), causal=True, window=1024, sink=True, sm_scale=S,
+                           seed=41), None),
 }
 
 
