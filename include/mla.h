@@ -119,7 +119,10 @@ int mla_device_num_cus(int32_t* num_cus);
  * topk entries) on the device and writes the int32 plan: a header, per-group split ranges,
  * per-unit split ranges, per-group (first row, row count), and split records (group, first block,
  * end block, unit), blocks being 64 consecutive effective rows; plus a zero row used for masked
- * rows. The plan stays valid until overwritten and may be reused by every layer of a forward. */
+ * rows and one 32-byte descriptor per split (group, request, first row, row count, request
+ * length, range of 32-row steps, the group's split count) from which a decode workgroup starts
+ * the split in one read. The plan stays valid until overwritten and may be reused by every layer
+ * of a forward. */
 int mla_decode_plan(const mla_problem* p, int32_t num_cus, const int32_t* seqlens,
                     const int32_t* topk_lens, void* plan, size_t plan_bytes, void* stream);
 

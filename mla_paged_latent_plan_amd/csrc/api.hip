@@ -186,6 +186,7 @@ int decode_impl(const mla_problem* p, int32_t num_cus, const void* q, const void
   a.unit_ptr_off = lay.unit_ptr;
   a.grp_rows_off = lay.grp_rows;
   a.splits_off = lay.splits;
+  a.sdesc_off = lay.sdesc_bytes_off / 4;
   a.B = sh.B;
   a.Sq = sh.Sq;
   a.H = sh.H;

@@ -974,18 +974,17 @@ struct Spec64 {
 
   __device__ __forceinline__ void load_split(int s) {
     cur_split = s;
-    const int32_t* plan = a.plan;
-    const int32_t* rec = plan + a.splits_off + 4 * (int64_t)s;
-    // split-wide values, kept in scalar registers (uniform across the workgroup)
-    g = __builtin_amdgcn_readfirstlane(rec[0]);
-    const int kb = __builtin_amdgcn_readfirstlane(rec[1]), ke = __builtin_amdgcn_readfirstlane(rec[2]);
-    j0 = __builtin_amdgcn_readfirstlane(plan[a.grp_rows_off + 2 * g]);
-    n = __builtin_amdgcn_readfirstlane(plan[a.grp_rows_off + 2 * g + 1]);
-    nsplit = __builtin_amdgcn_readfirstlane(plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g]);
-    b = (a.topk > 0) ? g / a.Sq : g;
-    L = __builtin_amdgcn_readfirstlane(a.seqlens[b]);
-    q0 = 2 * kb;
-    qend = min(2 * ke, (n + kRows - 1) / kRows);  // steps holding at least one row
+    // the split's descriptor (group, request, first row, rows, request length, step range, the
+    // group's split count), kept in scalar registers (uniform across the workgroup)
+    const int32_t* d = a.plan + a.sdesc_off + 8 * (int64_t)s;
+    g = __builtin_amdgcn_readfirstlane(d[0]);
+    b = __builtin_amdgcn_readfirstlane(d[1]);
+    j0 = __builtin_amdgcn_readfirstlane(d[2]);
+    n = __builtin_amdgcn_readfirstlane(d[3]);
+    L = __builtin_amdgcn_readfirstlane(d[4]);
+    q0 = __builtin_amdgcn_readfirstlane(d[5]);
+    qend = __builtin_amdgcn_readfirstlane(d[6]);  // steps holding at least one row
+    nsplit = __builtin_amdgcn_readfirstlane(d[7]);
   }
 
   // ===== score waves ===========================================================================
@@ -1544,25 +1543,12 @@ struct Tile128 {
     const int ln = lane_id();
     if (wave == 0 && ln < nc) {
       const int s = cb + ln;
-      const int32_t* plan = a.plan;
-      const int32_t* rec = plan + a.splits_off + 4 * (int64_t)s;
-      const int g = rec[0], kb = rec[1], ke = rec[2];
-      const int j0 = plan[a.grp_rows_off + 2 * g];
-      const int n = plan[a.grp_rows_off + 2 * g + 1];
-      const int ns = plan[a.grp_ptr_off + g + 1] - plan[a.grp_ptr_off + g];
-      const int b = sparse ? g / a.Sq : g;
-      const int L = a.seqlens[b];
-      const int q0 = 2 * kb;
-      const int qend = min(2 * ke, (n + kRows - 1) / kRows);  // steps holding at least one row
-      LDS_AS int* d = reinterpret_cast<LDS_AS int*>(sm + kDOff + 32 * ln);
-      d[D_G] = g;
-      d[D_B] = b;
-      d[D_J0] = j0;
-      d[D_N] = n;
-      d[D_L] = L;
-      d[D_Q0] = q0;
-      d[D_QEND] = qend;
-      d[D_NSPLIT] = ns;
+      // the plan's descriptor of the split, in the order of the D_ fields
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.plan + a.sdesc_off + 8 * (int64_t)s);
+      const u32x4 v0 = src[0], v1 = src[1];
+      LDS_AS u32x4* d = reinterpret_cast<LDS_AS u32x4*>(sm + kDOff + 32 * ln);
+      d[0] = v0;
+      d[1] = v1;
     }
   }
 

@@ -10,7 +10,8 @@ namespace mla {
 
 // ---- plan layout (int32 words) -------------------------------------------------------------
 // header[16] | grp_ptr[G+1] | unit_ptr[U+1] | grp_rows[2G] | splits[4*(G+U)] | pad to 256 B |
-// zero row (kZeroRowBytes)
+// zero row (kZeroRowBytes) | split descriptors [G+U][8]: (g, b, j0, n, L, q0, qend, nsplit) of
+// each split, everything a decode kernel needs to start it, in one 32-byte record
 constexpr int32_t kPlanMagic = 0x4D4C4131;
 constexpr int kHeaderWords = 16;
 constexpr int kBlockRows = 64;       // rows per block (one LDS stage)
@@ -23,7 +24,7 @@ enum { H_MAGIC = 0, H_G, H_U, H_S, H_R, H_MTILES, H_MTILE, H_QUOTA, H_FIXED, H_T
 struct PlanLayout {
   int64_t G, U;
   int64_t grp_ptr, unit_ptr, grp_rows, splits, words;  // word offsets
-  int64_t zero_row_bytes_off, bytes;                    // byte offsets / size
+  int64_t zero_row_bytes_off, sdesc_bytes_off, bytes;   // byte offsets / size
   static PlanLayout make(int64_t G, int64_t U) {
     PlanLayout l;
     l.G = G;
@@ -34,7 +35,8 @@ struct PlanLayout {
     l.splits = l.grp_rows + 2 * G;
     l.words = l.splits + 4 * (G + U);
     l.zero_row_bytes_off = ((l.words * 4 + 255) / 256) * 256;
-    l.bytes = l.zero_row_bytes_off + kZeroRowBytes;
+    l.sdesc_bytes_off = l.zero_row_bytes_off + kZeroRowBytes;
+    l.bytes = l.sdesc_bytes_off + 32 * (G + U);
     return l;
   }
 };
@@ -79,7 +81,7 @@ struct DecodeArgs {
   float* part_max;    // fp32 [S_max][R] per-split maxima; used only with max_logits
   int64_t page_stride, num_pages, row_bytes;
   int64_t scale_off;  // fp8 rows: byte offset of a page's scale slots (page_size * row_bytes)
-  int64_t grp_ptr_off, unit_ptr_off, grp_rows_off, splits_off;
+  int64_t grp_ptr_off, unit_ptr_off, grp_rows_off, splits_off, sdesc_off;
   int B, Sq, H, R, G, U, m_tiles, ps_log2, max_pages, topk, causal, window;
   float scale_log2;  // sm_scale * log2(e)
 };

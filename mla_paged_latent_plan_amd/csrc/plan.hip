@@ -124,6 +124,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         rec[1] = (int32_t)kb;
         rec[2] = (int32_t)ke;
         rec[3] = (int32_t)u;
+        // the split's descriptor: group, request, first row, rows, request length, step range
+        // (32-row steps holding at least one row), the group's split count
+        const int j0 = plan[lay.grp_rows + 2 * g], n = plan[lay.grp_rows + 2 * g + 1];
+        const int b = (a.topk > 0) ? g / a.Sq : g;
+        int4* d = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + lay.sdesc_bytes_off) + 2 * sp;
+        d[0] = make_int4(g, b, j0, n);
+        d[1] = make_int4(a.seqlens[b], 2 * (int)kb, min(2 * (int)ke, (n + 31) / 32), (int)(ul - uf + 1));
         ++sp;
       }
     }

@@ -124,6 +124,28 @@ def plan_words(wl, num_cus: int) -> np.ndarray:
     return oplan.build_plan(wl.seqlens, s.q_len, s.num_heads, num_cus, s.topk, s.window, tl)
 
 
+def check_split_descriptors(plan: torch.Tensor, want_words: np.ndarray, wl) -> None:
+    """The plan's per-split descriptors (after the padded words and the 2 KB zero row: one
+    32-byte record per split, (g, b, j0, n, L, q0, qend, nsplit)) against the oracle plan's words
+    they restate: the split record, the group's rows and split count, the request's length."""
+    s = wl.spec
+    w = np.asarray(want_words, dtype=np.int64)
+    G, U, S = int(w[1]), int(w[2]), int(w[3])
+    grp_ptr = w[16:16 + G + 1]
+    grp_rows = w[16 + G + 1 + U + 1:16 + G + 1 + U + 1 + 2 * G].reshape(G, 2)
+    recs = w[16 + G + 1 + U + 1 + 2 * G:][:4 * S].reshape(S, 4)
+    n_words = 16 + (G + 1) + (U + 1) + 2 * G + 4 * (G + U)
+    off = (n_words * 4 + 255) // 256 * 256 + 2048
+    got = plan.numpy()[off:off + 32 * S].view(np.int32).reshape(S, 8)
+    for sp in range(S):
+        g, kb, ke = int(recs[sp, 0]), int(recs[sp, 1]), int(recs[sp, 2])
+        j0, n = int(grp_rows[g, 0]), int(grp_rows[g, 1])
+        b = g // s.q_len if s.topk > 0 else g
+        want = [g, b, j0, n, int(wl.seqlens[b]), 2 * kb, min(2 * ke, -(-n // 32)),
+                int(grp_ptr[g + 1] - grp_ptr[g])]
+        assert got[sp].tolist() == want, f"split {sp}: descriptor {got[sp].tolist()} != {want}"
+
+
 def metrics(out: torch.Tensor, lse: torch.Tensor, O_ref: np.ndarray, L_ref: np.ndarray,
             A_ref: Optional[np.ndarray] = None) -> dict:
     """Error metrics of a GPU result against the oracle.

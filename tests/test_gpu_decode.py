@@ -112,6 +112,7 @@ def test_parity(name, cus):
     want = H.plan_words(wl, used)
     got = plan.view(torch.int32).numpy()[:len(want)]
     assert np.array_equal(got, want), f"plan differs for {name}/{cus}"
+    H.check_split_descriptors(plan, want, wl)
 
 
 def test_page_permutation_bitwise():
@@ -201,6 +202,7 @@ def test_full_size_configs(cfg):
     H.assert_parity(m, ctx=f"config {cfg}", scaled=H.scaled_bound(wl))
     want = H.plan_words(wl, used)
     assert np.array_equal(plan.view(torch.int32).numpy()[:len(want)], want)
+    H.check_split_descriptors(plan, want, wl)
 
 
 def test_graph_replay_matches_eager():
@@ -265,6 +267,7 @@ def test_maximum_sizes(case):
     H.assert_parity(m, ctx=case, scaled=H.scaled_bound(wl))
     want = H.plan_words(wl, used)
     assert np.array_equal(plan.view(torch.int32).numpy()[:len(want)], want)
+    H.check_split_descriptors(plan, want, wl)
 
 
 def test_sparse_duplicate_indices_count_per_occurrence():
