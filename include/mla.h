@@ -308,6 +308,22 @@ const char* mla_strerror(int status);
  * built without it). A caller compares it with the same hash of the sources it expects. */
 const char* mla_build_id(void);
 
+/* Checked mode (the data contract of mla_decode made visible). With checks on, every mla_decode,
+ * mla_decode_noalloc and mla_sparse_prefill call first runs a validation kernel on its stream that
+ * sets bits of a per-device word, instead of the decode silently reading zero rows:
+ *   MLA_CHECK_PAGE    a block-table entry outside [0, num_pages) for a page holding a row the
+ *                     call attends to (dense: the request's rows or its window's; index lists:
+ *                     a listed position in [0, L) within the token's row count)
+ *   MLA_CHECK_LENGTH  such a row past the block table (page index >= max_pages_per_seq)
+ *   MLA_CHECK_PLAN    a plan whose header does not describe the problem and CU count
+ * The decode itself runs unchanged. mla_check_enable sets the process-wide switch (default off;
+ * returns MLA_OK). mla_check_status waits for the stream's work, writes the current device's bits
+ * to *bits (host pointer) and clears them when clear != 0; MLA_ERR_NULL for a NULL bits,
+ * MLA_ERR_DEVICE if the read fails. Calls that overlap on one device share its word. */
+enum { MLA_CHECK_PAGE = 1, MLA_CHECK_LENGTH = 2, MLA_CHECK_PLAN = 4 };
+int mla_check_enable(int32_t on);
+int mla_check_status(uint32_t* bits, int32_t clear, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

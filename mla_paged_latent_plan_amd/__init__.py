@@ -58,6 +58,20 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+MLA_CHECK_PAGE, MLA_CHECK_LENGTH, MLA_CHECK_PLAN = 1, 2, 4
+
+
+def mla_check_enable(on: bool) -> None:
+    """Checked mode for every later decode call: a validation kernel records contract violations
+    (MLA_CHECK_* bits) in a per-device word (include/mla.h, mla_check_enable)."""
+    _lib.check_enable(on)
+
+
+def mla_check_status(clear: bool = True, stream=None) -> int:
+    """The current device's MLA_CHECK_* bits once the stream's work is done (mla_check_status)."""
+    return _lib.check_status(clear, _stream(stream))
+
+
 def mla_decode_plan(p: Problem, num_cus: int, seqlens: torch.Tensor,
                     topk_lens: Optional[torch.Tensor], plan: torch.Tensor, stream=None) -> None:
     lib = _lib.load()

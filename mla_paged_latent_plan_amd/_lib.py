@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = ("mla_get_workspace_size", "mla_device_num_cus", "mla_decode_plan", "mla_decode",
            "mla_combine", "mla_decode_noalloc", "mla_kv_write", "mla_q_absorb", "mla_v_up", "mla_swa_runs", "mla_gather_context", "mla_plan_context_chunks",
            "mla_sparse_prefill_workspace_size", "mla_sparse_prefill", "mla_build_id",
-           "mla_strerror")
+           "mla_check_enable", "mla_check_status", "mla_strerror")
 
 
 class MLAError(RuntimeError):
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        vp, sz, vp, vp, vp, vp]
     lib.mla_strerror.argtypes = [ctypes.c_int]
     lib.mla_strerror.restype = ctypes.c_char_p
+    lib.mla_check_enable.argtypes = [i32]
+    lib.mla_check_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32, vp]
     lib.mla_build_id.argtypes = []
     lib.mla_build_id.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -110,6 +112,19 @@ def workspace_size(p: Problem, num_cus: int):
     check("mla_get_workspace_size", lib.mla_get_workspace_size(ctypes.byref(p), num_cus,
                                                               ctypes.byref(a), ctypes.byref(b)))
     return a.value, b.value
+
+
+def check_enable(on: bool) -> None:
+    """Checked mode on or off for every later decode call (mla_check_enable)."""
+    check("mla_check_enable", load().mla_check_enable(1 if on else 0))
+
+
+def check_status(clear: bool, stream: int) -> int:
+    """The current device's checked-mode bits after the stream's work (mla_check_status)."""
+    bits = ctypes.c_uint32(0)
+    check("mla_check_status", load().mla_check_status(ctypes.byref(bits), 1 if clear else 0,
+                                                      ctypes.c_void_p(stream)))
+    return int(bits.value)
 
 
 def device_num_cus() -> int:

@@ -11,7 +11,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
-SOURCES = ["plan.hip", "decode.hip", "combine.hip", "kvwrite.hip", "absorb.hip", "swa_runs.hip", "gather.hip", "sparse_meta.hip", "api.hip"]
+SOURCES = ["plan.hip", "decode.hip", "combine.hip", "kvwrite.hip", "absorb.hip", "swa_runs.hip", "gather.hip", "sparse_meta.hip", "check.hip", "api.hip"]
 HEADERS = ["mla_internal.h", "layer_internal.h"]
 PUBLIC_HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "mla.h")
 

@@ -6,6 +6,7 @@
 
 #include <math.h>
 
+#include <atomic>
 #include <mutex>
 
 // Hash of the sources the library was built from (set by the build; see mla_build_id).
@@ -91,6 +92,8 @@ size_t partial_size(const Shape& sh) {
 }
 
 int launch_rc(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+std::atomic<bool> g_checked{false};  // checked mode (mla_check_enable)
 
 }  // namespace
 
@@ -200,6 +203,26 @@ int decode_impl(const mla_problem* p, int32_t num_cus, const void* q, const void
   a.causal = sh.causal;
   a.window = sh.window;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
+  if (g_checked.load(std::memory_order_relaxed)) {
+    mla::CheckArgs c;
+    c.plan = a.plan;
+    c.block_table = block_table;
+    c.seqlens = seqlens;
+    c.indices = a.indices;
+    c.num_pages = sh.num_pages;
+    c.grp_rows_off = lay.grp_rows;
+    c.B = sh.B;
+    c.Sq = sh.Sq;
+    c.R = sh.R;
+    c.G = sh.G;
+    c.U = sh.U;
+    c.ps_log2 = sh.ps_log2;
+    c.max_pages = sh.max_pages;
+    c.topk = sh.topk;
+    c.window = sh.window;
+    rc = launch_rc(mla::launch_check(c, static_cast<hipStream_t>(stream)));
+    if (rc != MLA_OK) return rc;
+  }
   return launch_rc(mla::launch_decode(a, sh, static_cast<hipStream_t>(stream)));
 }
 
@@ -594,6 +617,18 @@ int mla_plan_context_chunks(int32_t num_reqs, const int32_t* context_lens, int64
   return MLA_OK;
 }
 const char* mla_build_id(void) { return MLA_BUILD_ID; }
+
+int mla_check_enable(int32_t on) {
+  g_checked.store(on != 0, std::memory_order_relaxed);
+  return MLA_OK;
+}
+
+int mla_check_status(uint32_t* bits, int32_t clear, void* stream) {
+  if (bits == nullptr) return MLA_ERR_NULL;
+  return mla::check_status(bits, clear != 0, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_DEVICE;
+}
 
 const char* mla_strerror(int status) {
   switch (status) {

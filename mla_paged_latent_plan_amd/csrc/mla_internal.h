@@ -10,12 +10,15 @@ namespace mla {
 
 // ---- plan layout (int32 words) -------------------------------------------------------------
 // header[16] | grp_ptr[G+1] | unit_ptr[U+1] | grp_rows[2G] | splits[4*(G+U)] | pad to 256 B |
-// zero row (kZeroRowBytes) | split descriptors [G+U][8]: (g, b, j0, n, L, q0, qend, nsplit) of
+// zero rows (kZeroRowBytes) | split descriptors [G+U][8]: (g, b, j0, n, L, q0, qend, nsplit) of
 // each split, everything a decode kernel needs to start it, in one 32-byte record
 constexpr int32_t kPlanMagic = 0x4D4C4131;
 constexpr int kHeaderWords = 16;
 constexpr int kBlockRows = 64;       // rows per block (one LDS stage)
-constexpr int kZeroRowBytes = 2048;  // >= the widest row (1152 B)
+// Zero rows: eight of the widest row (1152 B), rounded up. The 128-row tile addresses row i of an
+// eight-row run as page base + i * row bytes (+ an offset inside the row), and an out-of-range
+// page entry gives the zero row as that base, so reads reach up to 8 rows past it.
+constexpr int kZeroRowBytes = 9472;
 constexpr int kMaxGroups = 8192;     // plan kernel keeps per-group state in LDS
 constexpr int kDv = 512;
 
@@ -145,10 +148,24 @@ struct KvWriteArgs {
   int ps_log2;
 };
 
+// Checked mode: the inputs of a decode call tested against the contract (csrc/check.hip).
+struct CheckArgs {
+  const int32_t* plan;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const int32_t* indices;  // index lists, or nullptr
+  int64_t num_pages;
+  int64_t grp_rows_off;    // plan words: (first row, row count) per group
+  int B, Sq, R, G, U, ps_log2, max_pages, topk, window;
+};
+
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, const Shape& sh, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_kv_write(const KvWriteArgs& a, int fmt, int d_nope, hipStream_t s);
+hipError_t launch_check(const CheckArgs& a, hipStream_t s);
+// The current device's checked-mode bits (after the stream's work), cleared on request.
+hipError_t check_status(uint32_t* bits, bool clear, hipStream_t s);
 
 }  // namespace mla

@@ -125,7 +125,7 @@ def plan_words(wl, num_cus: int) -> np.ndarray:
 
 
 def check_split_descriptors(plan: torch.Tensor, want_words: np.ndarray, wl) -> None:
-    """The plan's per-split descriptors (after the padded words and the 2 KB zero row: one
+    """The plan's per-split descriptors (after the padded words and 9472 bytes of zero rows: one
     32-byte record per split, (g, b, j0, n, L, q0, qend, nsplit)) against the oracle plan's words
     they restate: the split record, the group's rows and split count, the request's length."""
     s = wl.spec
@@ -135,7 +135,7 @@ def check_split_descriptors(plan: torch.Tensor, want_words: np.ndarray, wl) -> N
     grp_rows = w[16 + G + 1 + U + 1:16 + G + 1 + U + 1 + 2 * G].reshape(G, 2)
     recs = w[16 + G + 1 + U + 1 + 2 * G:][:4 * S].reshape(S, 4)
     n_words = 16 + (G + 1) + (U + 1) + 2 * G + 4 * (G + U)
-    off = (n_words * 4 + 255) // 256 * 256 + 2048
+    off = (n_words * 4 + 255) // 256 * 256 + 9472
     got = plan.numpy()[off:off + 32 * S].view(np.int32).reshape(S, 8)
     for sp in range(S):
         g, kb, ke = int(recs[sp, 0]), int(recs[sp, 1]), int(recs[sp, 2])

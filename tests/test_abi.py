@@ -57,8 +57,8 @@ def test_workspace_sizes(lib):
     assert rc == 0
     G, U = 2, 256
     words = 16 + (G + 1) + (U + 1) + 2 * G + 4 * (G + U)
-    # words, padded to 256 bytes, the 2 KB zero row, then a 32-byte descriptor per split slot
-    assert plan_b == ((words * 4 + 255) // 256) * 256 + 2048 + 32 * (G + U)
+    # words, padded to 256 bytes, 9472 bytes of zero rows, then a 32-byte descriptor per split slot
+    assert plan_b == ((words * 4 + 255) // 256) * 256 + 9472 + 32 * (G + U)
     assert part_b == (G + U) * 16 * (512 * 2 + 4)
     # 128 heads: one 128-row tile per group, U = cus
     rc, _, part_b = ws(good(num_heads=128), 256)
